@@ -1,0 +1,403 @@
+#!/usr/bin/env python3
+"""Benchmark of the SiLU-gated RMSNorm training forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7684x48]
+
+A step is one training forward and backward over the workload: the forward
+(y from x, g, w) followed by the backward (dx, dg and the deterministic BF16
+dw, one kernel).  W untimed steps run first, then exactly K steps are timed
+with HIP events on the stream the kernels are launched on, bracketed by
+device synchronizations.  Inputs are synthetic (seeded) and resident in HBM
+when timing starts.
+
+Every timed loop rotates over several identical buffer sets (inputs copied,
+outputs and workspace separate) that together span at least 1 GiB per
+tensor role, four times the 256 MB Infinity Cache: a launch never finds its
+inputs left in a cache by the previous launch, so the figures are HBM
+figures.  Within one step the backward may still find part of x and g that
+its forward just read; that reuse is the step's own.
+
+stdout gets one JSON line; everything else goes to stderr.  Besides the step
+throughput the line carries per-operation timings (eager and graph
+replayed), the roofline of the dominant kernel (the backward) against
+MI355X's 8 TB/s HBM peak, and the FP64 CPU oracle timed on the host cores
+("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+D = 128
+ROW_BYTES = D * 2               # one BF16 row
+ROTATION_BYTES = 1 << 30        # per tensor role, across the buffer sets
+
+# The pages' own timings of the same operations at T x H = 7684 x 48 on an
+# NVIDIA R200 (sm_107a, 212 SMs, CUDA 13.4): flashinfer PR #8701, Table 2
+# ("new us" and the deterministic package's column).  Context only.
+R200_7684x48_US = {
+    "fwd": 30.672, "fwdg": 30.553, "bwdg": 59.872, "bwdg_f32": 59.744,
+    "ckptg": 118.449, "stepg_f32": 118.537, "fwd+bwd": 90.424,
+    "det_fwd": 34.641, "det_bwdg": 65.896, "det_ckptg": 132.328,
+}
+
+COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
+KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="7684x48")
+    p.add_argument("--op-reps", type=int, default=50,
+                   help="launches per operation in the per-op timings")
+    p.add_argument("--no-ops", action="store_true", help="skip per-op timings")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time of the oracle baseline")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files "
+                        "(FETCH_SIZE, WRITE_SIZE) of this benchmark into the per-launch "
+                        "HBM traffic summary under profiles/")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, workload=args.workload)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this operator's hot path is measured on a "
+              "single MI355X (rows are independent; sharding across GPUs is a design "
+              "note, not part of this build). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+
+    from silu_gated_rmsnorm_amd import binding
+    from silu_gated_rmsnorm_amd.inputs import WORKLOADS, make_workload_inputs
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    wl = WORKLOADS[args.workload]
+    rows, eps = wl.rows, wl.eps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = binding.load_library()
+    tensor_bytes = rows * ROW_BYTES
+    nsets = math.ceil(ROTATION_BYTES / tensor_bytes) + 1
+    log(f"[bench] workload {wl.name}: rows={rows} D={D} eps={eps} "
+        f"buffer sets={nsets} lib={binding.library_path()}")
+
+    inp = make_workload_inputs(wl, device=dev)
+    ws_bytes = binding.gated_rmsnorm_workspace_bytes(rows)
+    sets = []
+    for _ in range(nsets):
+        st = {k: inp[k].clone() for k in ("x", "g", "dy")}
+        st["w"] = inp["w"]
+        for k in ("y", "dx", "dg"):
+            st[k] = torch.empty_like(inp["x"])
+        st["dw16"] = torch.empty(D, dtype=torch.bfloat16, device=dev)
+        st["dw32"] = torch.empty(D, dtype=torch.float32, device=dev)
+        st["ws"] = binding.new_workspace(rows, dev)
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    S = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    def check(status):
+        if status != 0:
+            raise RuntimeError(lib.gated_rmsnorm_status_string(status).decode())
+
+    # Raw C-ABI calls on buffer set `st` (no per-call Python checks).
+    def op_fwd(st):
+        check(lib.gated_rmsnorm_fwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["y"]), rows, D,
+                                    eps, 0, S()))
+
+    def op_bwd(st, fp32=False):
+        dw = st["dw32"] if fp32 else st["dw16"]
+        check(lib.gated_rmsnorm_bwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
+                                    P(st["dx"]), P(st["dg"]), P(dw), P(st["ws"]), ws_bytes,
+                                    rows, D, eps, 0, int(fp32), S()))
+
+    def op_ckpt(st, fp32=False):
+        dw = st["dw32"] if fp32 else st["dw16"]
+        check(lib.gated_rmsnorm_ckpt_step(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
+                                          P(st["y"]), P(st["dx"]), P(st["dg"]), P(dw),
+                                          P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32),
+                                          S()))
+
+    def op_step(st):
+        op_fwd(st)
+        op_bwd(st, False)
+
+    # Algorithmic bytes: what the method must move (inputs read once,
+    # outputs written once, w and dw included; workspace traffic, ~0.4 % of
+    # the backward's, is implementation overhead and not counted).
+    fwd_bytes = rows * 3 * ROW_BYTES + ROW_BYTES
+    bwd_bytes = rows * 5 * ROW_BYTES + ROW_BYTES + D * 2
+    bwd32_bytes = rows * 5 * ROW_BYTES + ROW_BYTES + D * 4
+    ckpt_bytes = 2 * fwd_bytes + bwd_bytes
+    ckpt32_bytes = 2 * fwd_bytes + bwd32_bytes
+    step_bytes = fwd_bytes + bwd_bytes
+
+    def rotate_time(fn, reps):
+        """Average µs per call over `reps` back-to-back calls, rotating sets."""
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            fn(sets[i % nsets])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    # ---- the contract measurement: K timed steps --------------------------
+    for i in range(args.warmup):
+        op_step(sets[i % nsets])
+    torch.cuda.synchronize()
+    step_us = rotate_time(op_step, args.steps)
+    ms_per_step = step_us / 1e3
+    value = step_bytes / (step_us * 1e-6) / 1e9
+    log(f"[bench] step (fwd + bwd, bf16 dw): {step_us:.2f} us, {value:.1f} GB/s "
+        f"({100 * value / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+
+    ops = {}
+    roofline = None
+    if not args.no_ops:
+        R = args.op_reps
+
+        def rec(name, us, nbytes):
+            gbps = nbytes / (us * 1e-6) / 1e9
+            ops[name] = {"us": round(us, 3), "GB/s": round(gbps, 1),
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            log(f"[bench] {name:18s} {us:9.2f} us {gbps:8.1f} GB/s "
+                f"{100 * gbps / HBM_PEAK_GBPS:5.1f}%")
+
+        for st in sets:
+            op_ckpt(st)
+        torch.cuda.synchronize()
+        rec("fwd", rotate_time(op_fwd, R), fwd_bytes)
+        bwd_us = rotate_time(op_bwd, R)
+        rec("bwd", bwd_us, bwd_bytes)
+        rec("bwd_f32", rotate_time(lambda st: op_bwd(st, True), R), bwd32_bytes)
+        rec("ckpt", rotate_time(op_ckpt, R), ckpt_bytes)
+        rec("ckpt_f32", rotate_time(lambda st: op_ckpt(st, True), R), ckpt32_bytes)
+        rec("fwd+bwd", step_us, step_bytes)
+
+        # Graph replays (the pages' fwdg / bwdg / ckptg / stepg_f32): one
+        # graph per buffer set, replayed in rotation.
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        kinds = {"fwdg": (op_fwd, fwd_bytes), "bwdg": (op_bwd, bwd_bytes),
+                 "bwdg_f32": (lambda st: op_bwd(st, True), bwd32_bytes),
+                 "ckptg": (op_ckpt, ckpt_bytes),
+                 "stepg_f32": (lambda st: op_ckpt(st, True), ckpt32_bytes)}
+        for name, (fn, nbytes) in kinds.items():
+            graphs = []
+            for st in sets:
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=s):
+                    fn(st)
+                graphs.append(gr)
+            for gr in graphs:
+                gr.replay()
+            torch.cuda.synchronize()
+            by_set = {id(st): gr for st, gr in zip(sets, graphs)}
+            rec(name, rotate_time(lambda st: by_set[id(st)].replay(), R), nbytes)
+            del graphs, by_set
+
+        # Same buffers every launch (no rotation): inputs partly served by the
+        # Infinity Cache; reported for contrast only.
+        one = sets[0]
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        for name, fn, nbytes in (("fwd_same_buffers", op_fwd, fwd_bytes),
+                                 ("bwd_same_buffers", op_bwd, bwd_bytes)):
+            fn(one)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(R):
+                fn(one)
+            b.record()
+            torch.cuda.synchronize()
+            rec(name, a.elapsed_time(b) * 1e3 / R, nbytes)
+
+        # Roofline of the dominant kernel: the backward is one kernel launch
+        # (rows > 0), timed over back-to-back launches on its stream.
+        per_launch = bwd_bytes
+        achieved = per_launch / (bwd_us * 1e-6) / 1e9
+        roofline = {"kernel": "grn::bwd_kernel<2>", "bound": "hbm",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic_from_counters(),
+                    "bytes_per_launch": per_launch, "avg_us": round(bwd_us, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wl, fwd_bytes + bwd_bytes, args.cpu_seconds)
+
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) + us, gated RMSNorm fwd/bwd at "
+                  f"{wl.name}x128 bf16",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic (seeded normal BF16 inputs resident in HBM)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "rows": rows, "D": D,
+                   "eps": eps, "step": "fwd + bwd (deterministic BF16 dw)",
+                   "bytes_per_step": step_bytes, "buffer_sets": nsets},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ops": ops,
+        "context_r200_us": R200_7684x48_US if wl.name == "7684x48" else None,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def traffic_from_counters():
+    """HBM bytes per launch of the backward kernel from committed counters.
+
+    The file is written from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
+    of this benchmark, each scaled by the same counter's reading on a copy of
+    known size.  It records the SHA-256 of the kernel source it was taken on;
+    if the source has changed since, the figure no longer applies (None).
+    """
+    try:
+        rec = json.loads(COUNTERS_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, summed counter value)} from a rocprofv3 CSV."""
+    import csv
+
+    out = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            d = r["Dispatch_Id"]
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, workload="7684x48"):
+    """Per-launch HBM bytes of the kernels, scaled by a copy of known size.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  The benchmark's
+    setup clones each input tensor with a plain device copy
+    (__amd_rocclr_copyBuffer) of exactly rows * 256 bytes; the ratio of that
+    size to what each counter reports for those copies is the counter's
+    scale factor, applied to the other kernels' readings.
+    """
+    import statistics
+
+    from silu_gated_rmsnorm_amd.inputs import WORKLOADS
+
+    wl = WORKLOADS[workload]
+    copy_bytes = wl.rows * ROW_BYTES
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def med(table, key):
+        vals = [v for (n, v) in table.values() if key in n]
+        return statistics.median(vals) if vals else None, len(vals)
+
+    cf, ncf = med(fetch, "copyBuffer")
+    cw, ncw = med(write, "copyBuffer")
+    if not cf or not cw:
+        sys.exit("no copy dispatches with counter values in the CSV files")
+    scale_f = copy_bytes / (cf * 1024)
+    scale_w = copy_bytes / (cw * 1024)
+    rows = wl.rows
+    alg = {"bwd_kernel": rows * 5 * ROW_BYTES + ROW_BYTES + D * 2,
+           "fwd_kernel": rows * 3 * ROW_BYTES + ROW_BYTES}
+    kernels = {}
+    for key in ("bwd_kernel", "fwd_kernel"):
+        f, nf = med(fetch, key)
+        w, nw = med(write, key)
+        if f is None or w is None:
+            continue
+        rd, wr = f * 1024 * scale_f, w * 1024 * scale_w
+        kernels[key] = {"fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
+                        "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
+                        "hbm_bytes_per_launch": round(rd + wr),
+                        "algorithmic_bytes": alg[key],
+                        "traffic_over_algorithmic": round((rd + wr) / alg[key], 4)}
+    sha = hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+    rec = {"workload": workload, "kernel_source_sha256": sha,
+           "copy_bytes": copy_bytes, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+           "copy_dispatches": [ncf, ncw],
+           "fetch_scale": round(scale_f, 6), "write_scale": round(scale_w, 6),
+           "kernels": kernels,
+           "hbm_bytes_per_launch": kernels.get("bwd_kernel", {}).get("hbm_bytes_per_launch")}
+    COUNTERS_FILE.parent.mkdir(exist_ok=True)
+    COUNTERS_FILE.write_text(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
+def cpu_baseline(inp, wl, bytes_per_pass, min_seconds):
+    """Time the FP64 oracle (fwd + bwd incl. dw) on the whole workload."""
+    import oracle
+    from silu_gated_rmsnorm_amd.inputs import bf16_bits
+
+    b = {k: bf16_bits(v) for k, v in inp.items()}
+    threads = oracle.num_threads()
+    reps, total = 0, 0.0
+    while total < min_seconds:
+        t0 = time.perf_counter()
+        oracle.fwd(b["x"], b["g"], b["w"], wl.eps)
+        oracle.bwd(b["x"], b["g"], b["w"], b["dy"], wl.eps)
+        total += time.perf_counter() - t0
+        reps += 1
+    gbps = bytes_per_pass * reps / total / 1e9
+    log(f"[bench] cpu oracle: {reps} x fwd+bwd over {wl.rows} rows in {total:.1f} s, "
+        f"{gbps:.2f} GB/s on {threads} threads")
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {wl.name} workload ({wl.rows} rows), fwd + bwd with dw, "
+                      f"repeated {reps} times ({total:.1f} s)",
+            "seconds_per_pass": round(total / reps, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * gated_rmsnorm.h - C ABI of the MI355X (gfx950) SiLU-gated RMSNorm
+ * training forward and backward.
+ *
+ * The operator is the "SiLU-gated RMSNorm" training kernel of flashinfer
+ * PR #8701, "perf(cake_rmsnorm_silu_gate_train): L2-prefetching extra-long
+ * forward on SM107".  Its PR description names a forward and a backward
+ * with an optional FP32 weight gradient and a deterministic variant; its
+ * commit 10c6017 message names the inputs x and the gate z (called g here)
+ * with rows packed; "How the tables were measured" gives BF16 inputs, the
+ * operations fwd, bwd (BF16 or FP32 dw) and the checkpointed step
+ * (2 x forward + backward).  Per row i of D values, with a weight w of D
+ * values shared by all rows:
+ *
+ *     r_i  = 1 / sqrt(mean_j(x_ij^2) + eps)
+ *     y_ij = x_ij * r_i * w_j * silu(g_ij),    silu(v) = v / (1 + exp(-v))
+ *
+ * and the backward of L = sum(dy * y) gives dx, dg (per row) and
+ * dw_j = sum_i dy_ij * x_ij * r_i * silu(g_ij).  The determinism rule of
+ * the same kernel family (flashinfer PR #8878, commit message: weight
+ * gradients are accumulated in FP32 in one fixed order so that repeated runs
+ * agree bit for bit) is applied to dw here: dw is bit-identical from run to
+ * run and does not depend on the launch grid.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Layout: every activation (x, g, dy, y, dx, dg) is a row-major
+ *    [rows, D] array with rows packed (row stride = D elements).  w is [D].
+ *  - dtype: GRN_DTYPE_BF16 is the only accepted element type.  Arithmetic is
+ *    FP32; each BF16 output is rounded once, to nearest even.
+ *  - D: only D = 128 is accepted (one row = 256 bytes).
+ *  - rows: 0 <= rows <= GRN_MAX_ROWS.  rows = 0 is allowed: the forward does
+ *    nothing, the backward writes dw = 0 (an empty sum).  Activation pointers
+ *    may then be NULL.
+ *  - Memory: every pointer is device memory of the device that owns
+ *    `stream`.  The caller owns every buffer; the library allocates nothing,
+ *    keeps no pointer after returning and never synchronizes.  Work is only
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream), so
+ *    the calls may be captured into a HIP graph.
+ *  - Alignment: activations, w and the workspace must be 16-byte aligned;
+ *    dw 4-byte aligned (FP32) or 2-byte aligned (BF16).
+ *  - Aliasing: no output may overlap any input, another output or the
+ *    workspace.  An in-place dx = x would let one workgroup overwrite rows
+ *    that another has not read yet; the review of flashinfer PR #8878
+ *    ("Follow-up" findings) reports that race for a sibling kernel.
+ *  - eps: finite and >= 0.
+ *  - Errors: arguments are checked before anything is enqueued; an invalid
+ *    call returns a non-zero grn_status and enqueues nothing.  A failed
+ *    launch returns GRN_ERR_HIP.  Nothing is thrown across the ABI.
+ *  - Threads: the library holds no mutable state; concurrent calls are safe
+ *    if they share no output or workspace.
+ *  - Launch shape: the environment variable GATED_RMSNORM_MAX_WG, when set
+ *    to a positive integer, caps the number of workgroups per launch (a
+ *    tuning and testing knob).  Results do not depend on it.
+ */
+#ifndef GATED_RMSNORM_H
+#define GATED_RMSNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum grn_status {
+    GRN_OK = 0,
+    GRN_ERR_NULL = 1,      /* a required pointer is NULL                     */
+    GRN_ERR_SHAPE = 2,     /* D != 128, rows < 0 or rows > GRN_MAX_ROWS      */
+    GRN_ERR_DTYPE = 3,     /* dtype is not BF16, or dw_fp32 is not 0 or 1    */
+    GRN_ERR_ALIGN = 4,     /* a pointer is not aligned as required           */
+    GRN_ERR_ALIAS = 5,     /* an output overlaps an input, output or ws      */
+    GRN_ERR_WORKSPACE = 6, /* workspace missing or smaller than required     */
+    GRN_ERR_EPS = 7,       /* eps is negative, infinite or NaN               */
+    GRN_ERR_HIP = 8        /* the HIP runtime reported a launch error        */
+} grn_status;
+
+enum { GRN_DTYPE_BF16 = 0 };
+
+#define GRN_MAX_ROWS ((int64_t)2147483647)
+
+/* Bytes of device workspace the backward needs for `rows` rows of width D:
+ * a fixed region of arrival counters, one FP32 partial dw of D values per
+ * chunk of gated_rmsnorm_chunk_rows() rows, and one per group of about
+ * sqrt(chunks) chunks.  Returns 0 for rows <= 0 or an unsupported D.
+ *
+ * Workspace contract: the counter region must be zero before the first
+ * backward that uses the workspace (see gated_rmsnorm_workspace_init);
+ * every backward returns the counters it used to zero before it completes,
+ * so the same workspace then serves any later call of any size.  The rest
+ * of the workspace is scratch.  Two calls in flight at the same time must
+ * not share a workspace. */
+size_t gated_rmsnorm_workspace_bytes(int64_t rows, int32_t D);
+
+/* Number of rows in one dw chunk: rows [c*R, (c+1)*R) form chunk c. */
+int32_t gated_rmsnorm_chunk_rows(void);
+
+/* Forward: y = x * rsqrt(mean(x^2) + eps) * w * silu(g), row by row.
+ * In:  x, g [rows, D] BF16; w [D] BF16.   Out: y [rows, D] BF16.
+ * y of a row depends only on that row, w and eps: it is bitwise the same
+ * whatever the launch shape. */
+grn_status gated_rmsnorm_fwd(const void *x, const void *g, const void *w,
+                             void *y, int64_t rows, int32_t D, float eps,
+                             int32_t dtype, void *stream);
+
+/* Backward of L = sum(dy * y) (r is recomputed from x; nothing is saved by
+ * the forward):
+ *   dx = r (dn - n c),  n = x r,  dn = dy w silu(g),  c = mean_j(dn n)
+ *   dg = dy w n silu'(g)
+ *   dw = sum over rows of dy n silu(g)          (overwritten, not added to)
+ * In:  x, g, dy [rows, D] BF16; w [D] BF16; workspace of at least
+ *      gated_rmsnorm_workspace_bytes(rows, D) bytes whose counter region is
+ *      zero (see the workspace contract above; may be NULL when rows = 0).
+ * Out: dx, dg [rows, D] BF16; dw [D], FP32 if dw_fp32 = 1, else BF16.
+ * dw is summed in FP32 in a fixed order that depends only on rows (per
+ * chunk of rows, then per group of chunks, then over groups): it is
+ * bit-identical from run to run and across launch shapes.  The whole
+ * backward is one kernel launch (two dependent kernels never run). */
+grn_status gated_rmsnorm_bwd(const void *x, const void *g, const void *w,
+                             const void *dy, void *dx, void *dg, void *dw,
+                             void *workspace, size_t workspace_bytes,
+                             int64_t rows, int32_t D, float eps,
+                             int32_t dtype, int32_t dw_fp32, void *stream);
+
+/* The checkpointed training step: forward, forward again (recompute, into
+ * the same y), then the backward, enqueued in that order on `stream`.
+ * Arguments are those of gated_rmsnorm_fwd and gated_rmsnorm_bwd together;
+ * y must not overlap any other buffer.  Outputs are bitwise those of
+ * gated_rmsnorm_fwd followed by gated_rmsnorm_bwd. */
+grn_status gated_rmsnorm_ckpt_step(const void *x, const void *g,
+                                   const void *w, const void *dy, void *y,
+                                   void *dx, void *dg, void *dw,
+                                   void *workspace, size_t workspace_bytes,
+                                   int64_t rows, int32_t D, float eps,
+                                   int32_t dtype, int32_t dw_fp32,
+                                   void *stream);
+
+/* Zero the arrival counters at the front of a workspace (the first
+ * gated_rmsnorm_workspace_init_bytes() bytes) by enqueueing a small kernel
+ * on `stream`.  A workspace must be zero-filled, by this call or by any
+ * other means (e.g. hipMemset), once before its first use by
+ * gated_rmsnorm_bwd or gated_rmsnorm_ckpt_step.  Errors: NULL workspace ->
+ * GRN_ERR_NULL; fewer bytes than the counters need -> GRN_ERR_WORKSPACE;
+ * not 16-byte aligned -> GRN_ERR_ALIGN. */
+grn_status gated_rmsnorm_workspace_init(void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
+/* Size of the counter region that gated_rmsnorm_workspace_init zeroes. */
+size_t gated_rmsnorm_workspace_init_bytes(void);
+
+/* Static description of a status code (never NULL). */
+const char *gated_rmsnorm_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GATED_RMSNORM_H */

@@ -11,8 +11,9 @@
  * PR #8701, "perf(cake_rmsnorm_silu_gate_train): L2-prefetching
  * extra-long forward on SM107" (PR description: the training kernel with a
  * forward and a backward; commit 10c6017 message: inputs x and the gate z,
- * rows packed; "How the tables were measured": BF16 inputs, "the FP32
- * formula", a BF16 or an FP32 weight gradient).  The page prints no formula.
+ * rows packed; "How the tables were measured": BF16 inputs, a comparator
+ * that evaluates the formula in FP32, a BF16 or an FP32 weight gradient).
+ * The page prints no formula.
  * The plainest reading of the name, used here, normalises each row of D
  * values by its root mean square, scales by a weight w shared by all rows,
  * and gates elementwise with SiLU of z (called g below):

@@ -1,0 +1,195 @@
+"""Thin Python binding of ``libgated_rmsnorm.so`` (C ABI in include/gated_rmsnorm.h).
+
+Argument marshalling only: each function checks torch-level facts the C ABI
+cannot see (device, dtype, contiguity, shapes), passes raw device pointers
+and torch's current HIP stream, and turns a non-zero status into
+``GatedRMSNormError``.  Every step of the computation runs in the HIP
+kernels; there is no fallback: if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import threading
+
+import torch
+
+_PKG = pathlib.Path(__file__).resolve().parent
+_LIB_NAME = "libgated_rmsnorm.so"
+_lock = threading.Lock()
+_lib = None
+
+GRN_DTYPE_BF16 = 0
+D_SUPPORTED = 128
+
+
+class GatedRMSNormError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> pathlib.Path:
+    return _PKG / _LIB_NAME
+
+
+# Every symbol the header declares, with its ctypes signature.
+_VP = ctypes.c_void_p
+_SIGS = {
+    "gated_rmsnorm_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "gated_rmsnorm_chunk_rows": (ctypes.c_int32, []),
+    "gated_rmsnorm_fwd": (ctypes.c_int32, [_VP, _VP, _VP, _VP, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_float,
+                                            ctypes.c_int32, _VP]),
+    "gated_rmsnorm_bwd": (ctypes.c_int32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            ctypes.c_size_t, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_float,
+                                            ctypes.c_int32, ctypes.c_int32, _VP]),
+    "gated_rmsnorm_ckpt_step": (ctypes.c_int32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                  _VP, _VP, ctypes.c_size_t,
+                                                  ctypes.c_int64, ctypes.c_int32,
+                                                  ctypes.c_float, ctypes.c_int32,
+                                                  ctypes.c_int32, _VP]),
+    "gated_rmsnorm_workspace_init": (ctypes.c_int32, [_VP, ctypes.c_size_t, _VP]),
+    "gated_rmsnorm_workspace_init_bytes": (ctypes.c_size_t, []),
+    "gated_rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+}
+
+
+def load_library(path=None) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = pathlib.Path(path) if path is not None else library_path()
+        if not p.exists():
+            raise RuntimeError(
+                f"{p} is missing: build it with `python -m silu_gated_rmsnorm_amd.build`"
+                " (the HIP kernels are the only implementation)")
+        lib = ctypes.CDLL(str(p))
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().gated_rmsnorm_status_string(status).decode()
+        raise GatedRMSNormError(status, msg)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _act(name: str, t: torch.Tensor, rows=None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name}: expected a GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name}: expected bfloat16, got {t.dtype}")
+    if t.dim() != 2 or t.shape[1] != D_SUPPORTED:
+        raise ValueError(f"{name}: expected shape [rows, {D_SUPPORTED}], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: rows must be packed (contiguous)")
+    if rows is not None and t.shape[0] != rows:
+        raise ValueError(f"{name}: expected {rows} rows, got {t.shape[0]}")
+    return t.data_ptr()
+
+
+def _weight(w: torch.Tensor) -> int:
+    if not isinstance(w, torch.Tensor) or w.device.type != "cuda":
+        raise TypeError("w: expected a GPU tensor")
+    if w.dtype != torch.bfloat16 or w.shape != (D_SUPPORTED,) or not w.is_contiguous():
+        raise ValueError(f"w: expected a contiguous bfloat16 [{D_SUPPORTED}] tensor")
+    return w.data_ptr()
+
+
+def gated_rmsnorm_workspace_bytes(rows: int, D: int = D_SUPPORTED) -> int:
+    return int(load_library().gated_rmsnorm_workspace_bytes(rows, D))
+
+
+def new_workspace(rows: int, device) -> torch.Tensor:
+    """A zero-filled workspace for the backward of `rows` rows (or fewer).
+
+    Its arrival counters start at zero and every backward leaves them at
+    zero, so one workspace can be reused by later calls of any size up to
+    `rows`."""
+    need = max(gated_rmsnorm_workspace_bytes(rows), 16)
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
+def gated_rmsnorm_workspace_init(workspace: torch.Tensor) -> None:
+    """Zero the arrival counters of a workspace (enqueued on the current stream)."""
+    lib = load_library()
+    _check(lib.gated_rmsnorm_workspace_init(workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(workspace)))
+
+
+def _workspace(rows, device, workspace):
+    if workspace is None:
+        # one extra allocation per call; pass a workspace to avoid it
+        workspace = new_workspace(rows, device)
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace: expected a contiguous tensor on the inputs' device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gated_rmsnorm_fwd(x, g, w, eps: float = 1e-6, y=None):
+    """y = x * rsqrt(mean(x^2) + eps) * w * silu(g) row by row; returns y."""
+    lib = load_library()
+    rows = x.shape[0]
+    px, pg, pw = _act("x", x), _act("g", g, rows), _weight(w)
+    if y is None:
+        y = torch.empty_like(x)
+    py = _act("y", y, rows)
+    _check(lib.gated_rmsnorm_fwd(px, pg, pw, py, rows, D_SUPPORTED, float(eps),
+                                 GRN_DTYPE_BF16, _stream(x)))
+    return y
+
+
+def gated_rmsnorm_bwd(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
+                      dx=None, dg=None, dw=None, workspace=None):
+    """Gradients of sum(dy * y): returns (dx, dg, dw); dw is FP32 if dw_fp32."""
+    lib = load_library()
+    rows = x.shape[0]
+    px, pg, pw, pdy = _act("x", x), _act("g", g, rows), _weight(w), _act("dy", dy, rows)
+    dx = torch.empty_like(x) if dx is None else dx
+    dg = torch.empty_like(x) if dg is None else dg
+    dw_dtype = torch.float32 if dw_fp32 else torch.bfloat16
+    dw = torch.empty(D_SUPPORTED, dtype=dw_dtype, device=x.device) if dw is None else dw
+    if dw.dtype != dw_dtype or dw.shape != (D_SUPPORTED,) or dw.device != x.device:
+        raise ValueError(f"dw: expected a {dw_dtype} [{D_SUPPORTED}] tensor on the inputs' device")
+    ws, ws_bytes = _workspace(rows, x.device, workspace)
+    _check(lib.gated_rmsnorm_bwd(px, pg, pw, pdy, _act("dx", dx, rows), _act("dg", dg, rows),
+                                 dw.data_ptr(), ws.data_ptr(), ws_bytes, rows,
+                                 D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
+                                 int(bool(dw_fp32)), _stream(x)))
+    return dx, dg, dw
+
+
+def gated_rmsnorm_ckpt_step(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
+                            y=None, dx=None, dg=None, dw=None, workspace=None):
+    """Forward, recomputed forward, backward: returns (y, dx, dg, dw)."""
+    lib = load_library()
+    rows = x.shape[0]
+    px, pg, pw, pdy = _act("x", x), _act("g", g, rows), _weight(w), _act("dy", dy, rows)
+    y = torch.empty_like(x) if y is None else y
+    dx = torch.empty_like(x) if dx is None else dx
+    dg = torch.empty_like(x) if dg is None else dg
+    dw_dtype = torch.float32 if dw_fp32 else torch.bfloat16
+    dw = torch.empty(D_SUPPORTED, dtype=dw_dtype, device=x.device) if dw is None else dw
+    if dw.dtype != dw_dtype or dw.shape != (D_SUPPORTED,) or dw.device != x.device:
+        raise ValueError(f"dw: expected a {dw_dtype} [{D_SUPPORTED}] tensor on the inputs' device")
+    ws, ws_bytes = _workspace(rows, x.device, workspace)
+    _check(lib.gated_rmsnorm_ckpt_step(px, pg, pw, pdy, _act("y", y, rows),
+                                       _act("dx", dx, rows), _act("dg", dg, rows),
+                                       dw.data_ptr(), ws.data_ptr(), ws_bytes, rows,
+                                       D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
+                                       int(bool(dw_fp32)), _stream(x)))
+    return y, dx, dg, dw

@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (no argument checking here:
+// the C-ABI layer validates every argument before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace grn {
+
+// Rows per dw chunk.  The backward adds the dw contributions of chunk
+// [c*kChunkRows, (c+1)*kChunkRows) into one FP32 partial; the chunking, and
+// therefore the bits of dw, depend only on the number of rows.
+#ifndef GRN_CHUNK_ROWS
+#define GRN_CHUNK_ROWS 128
+#endif
+constexpr int kChunkRows = GRN_CHUNK_ROWS;
+
+// Workspace of the backward, in this order:
+//   counters  uint32[kCounterWords]  arrival counters (zero between calls)
+//   partial   float[nchunks][128]     one dw partial per chunk
+//   gpart     float[ngroups][128]     one dw partial per group of chunks
+constexpr int kMaxGroups = 8191;
+constexpr int kCounterWords = kMaxGroups + 1;
+constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
+
+struct BwdLayout {
+  int64_t nchunks = 0;
+  int64_t group_size = 1;
+  int64_t ngroups = 0;
+  size_t partial_off = 0;
+  size_t gpart_off = 0;
+  size_t bytes = 0;
+};
+
+BwdLayout bwd_layout(int64_t rows);
+
+hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
+                      int64_t rows, float eps, int max_wg, hipStream_t s);
+
+hipError_t launch_bwd(const void* x, const void* g, const void* w,
+                      const void* dy, void* dx, void* dg, void* dw,
+                      int dw_fp32, void* workspace, int64_t rows, float eps,
+                      int max_wg, hipStream_t s);
+
+hipError_t launch_counters_zero(void* workspace, hipStream_t s);
+
+}  // namespace grn

@@ -1,0 +1,124 @@
+"""Run-to-run and launch-shape determinism on the GPU.
+
+dw is summed in a fixed order that depends only on the number of rows, so
+it must be bit-identical over repeated runs (with the workspace poisoned
+between runs) and under any cap on the number of workgroups.  y, dx and dg
+depend on their row only and must be bitwise stable too.  The checkpointed
+step must give the same bits as fwd + bwd, and one workspace must serve
+calls of any size (its counters return to zero).
+"""
+import os
+
+import pytest
+import torch
+
+from silu_gated_rmsnorm_amd import binding
+from silu_gated_rmsnorm_amd.inputs import WORKLOADS, make_inputs, make_workload_inputs
+
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bwd_once(inp, eps, dw_fp32, ws):
+    ws.fill_(float("nan"))                 # poison the scratch ...
+    binding.gated_rmsnorm_workspace_init(ws)  # ... and zero the counters only
+    dx, dg, dw = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], eps,
+                                           dw_fp32=dw_fp32, workspace=ws)
+    torch.cuda.synchronize()
+    return dx, dg, dw
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["7684x48", "262144x48_outliers"])
+def test_dw_bitwise_over_10_runs(name):
+    wl = WORKLOADS[name]
+    say(f"[determinism] {name} 10 runs")
+    inp = make_workload_inputs(wl, device="cuda")
+    ws = torch.empty(binding.gated_rmsnorm_workspace_bytes(wl.rows) // 4, device="cuda")
+    modes = (True, False) if wl.rows < 10**6 else (True,)
+    for dw_fp32 in modes:
+        dx0, dg0, dw0 = _bwd_once(inp, wl.eps, dw_fp32, ws)
+        dx0, dg0, dw0 = dx0.clone(), dg0.clone(), dw0.clone()
+        for _ in range(9):
+            dx, dg, dw = _bwd_once(inp, wl.eps, dw_fp32, ws)
+            assert _same(dw, dw0)
+            assert _same(dx, dx0) and _same(dg, dg0)
+
+
+@pytest.mark.parametrize("rows", [49488, 1031, 257])
+def test_launch_shape_invariance(rows, monkeypatch):
+    say(f"[determinism] grid caps rows={rows}")
+    inp = make_inputs(rows, seed=3, device="cuda")
+    outs = []
+    for cap in (None, "1", "7", "64"):
+        if cap is None:
+            monkeypatch.delenv("GATED_RMSNORM_MAX_WG", raising=False)
+        else:
+            monkeypatch.setenv("GATED_RMSNORM_MAX_WG", cap)
+        y = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
+        dx, dg, dw = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"],
+                                               1e-6, dw_fp32=True)
+        torch.cuda.synchronize()
+        outs.append((y, dx, dg, dw))
+    monkeypatch.delenv("GATED_RMSNORM_MAX_WG", raising=False)
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert _same(a, b)
+
+
+@pytest.mark.parametrize("dw_fp32", [True, False])
+def test_ckpt_step_equals_fwd_then_bwd(dw_fp32):
+    rows = 9999
+    say(f"[determinism] ckpt vs fwd+bwd rows={rows} dw_fp32={dw_fp32}")
+    inp = make_inputs(rows, seed=5, device="cuda")
+    y1 = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
+    dx1, dg1, dw1 = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], 1e-6,
+                                              dw_fp32=dw_fp32)
+    y2, dx2, dg2, dw2 = binding.gated_rmsnorm_ckpt_step(inp["x"], inp["g"], inp["w"],
+                                                        inp["dy"], 1e-6, dw_fp32=dw_fp32)
+    torch.cuda.synchronize()
+    for a, b in ((y1, y2), (dx1, dx2), (dg1, dg2), (dw1, dw2)):
+        assert _same(a, b)
+
+
+def test_workspace_reused_across_sizes():
+    """The counters return to zero after each call: one workspace serves
+    calls of different sizes in any order, with the same bits as fresh ones."""
+    big, small = 70000, 3001
+    say(f"[determinism] workspace reuse rows={big},{small}")
+    a = make_inputs(big, seed=9, device="cuda")
+    b = make_inputs(small, seed=10, device="cuda")
+    ws = binding.new_workspace(big, "cuda")
+    outs = []
+    for inp in (a, b, a, b, b, a):
+        outs.append(binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], 1e-6,
+                                              dw_fp32=True, workspace=ws))
+    torch.cuda.synchronize()
+    fresh_a = binding.gated_rmsnorm_bwd(a["x"], a["g"], a["w"], a["dy"], 1e-6, dw_fp32=True)
+    fresh_b = binding.gated_rmsnorm_bwd(b["x"], b["g"], b["w"], b["dy"], 1e-6, dw_fp32=True)
+    torch.cuda.synchronize()
+    for out, ref in zip(outs, (fresh_a, fresh_b, fresh_a, fresh_b, fresh_b, fresh_a)):
+        for x, y in zip(out, ref):
+            assert _same(x, y)
+    C = binding.load_library().gated_rmsnorm_workspace_init_bytes()
+    assert torch.count_nonzero(ws[:C]).item() == 0
+
+
+def test_nondefault_stream():
+    rows = 3000
+    say(f"[determinism] side stream rows={rows}")
+    inp = make_inputs(rows, seed=8, device="cuda")
+    ref = binding.gated_rmsnorm_ckpt_step(inp["x"], inp["g"], inp["w"], inp["dy"], 1e-6, True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = binding.gated_rmsnorm_ckpt_step(inp["x"], inp["g"], inp["w"], inp["dy"], 1e-6,
+                                              True)
+    s.synchronize()
+    for a, b in zip(ref, out):
+        assert _same(a, b)

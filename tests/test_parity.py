@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path against the FP64 oracle, element by element.
+
+Small and ragged row counts (spanning several workgroup tiles, dw chunks and
+a partial tail), the 1031x48 workload in full, special values, empty input,
+and the four larger workloads at full size on sampled rows (y, dx, dg) with
+dw against the oracle's sum over every row.  Tolerances are in _compare.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from silu_gated_rmsnorm_amd import binding
+from silu_gated_rmsnorm_amd.inputs import WORKLOADS, make_inputs, make_workload_inputs
+
+from gpu_util import (assert_acts_close, assert_dw_close, bits, f64, gpu_all,
+                      oracle_all, say)
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 15, 16, 17, 31, 63, 64, 65, 255, 256,
+                                  257, 511, 513, 1000, 4099, 12345])
+def test_small_and_ragged(rows):
+    say(f"[parity] ragged rows={rows}")
+    inp = make_inputs(rows, seed=rows, device="cuda")
+    y_ref, dx_ref, dg_ref, dw_ref = oracle_all(inp, EPS)
+    for dw_fp32 in (True, False):
+        y, dx, dg, dw = gpu_all(inp, EPS, dw_fp32)
+        assert_acts_close("y", y, y_ref)
+        assert_acts_close("dx", dx, dx_ref)
+        assert_acts_close("dg", dg, dg_ref)
+        assert_dw_close(dw, dw_ref, dw_fp32)
+
+
+def test_workload_1031x48_full():
+    wl = WORKLOADS["1031x48"]
+    say(f"[parity] {wl.name} rows={wl.rows} full")
+    inp = make_workload_inputs(wl, device="cuda")
+    y_ref, dx_ref, dg_ref, dw_ref = oracle_all(inp, wl.eps)
+    for dw_fp32 in (False, True):
+        y, dx, dg, dw = gpu_all(inp, wl.eps, dw_fp32)
+        ey = assert_acts_close("y", y, y_ref)
+        ex = assert_acts_close("dx", dx, dx_ref)
+        eg = assert_acts_close("dg", dg, dg_ref)
+        ew = assert_dw_close(dw, dw_ref, dw_fp32)
+        say(f"  dw_fp32={dw_fp32}: y {ey:.2e} dx {ex:.2e} dg {eg:.2e} dw {ew}")
+
+
+def test_empty_rows():
+    say("[parity] rows=0")
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(128, dtype=torch.bfloat16, device="cuda")
+    y = binding.gated_rmsnorm_fwd(x, x, w, EPS)
+    assert y.shape == (0, 128)
+    for dw_fp32 in (True, False):
+        dw = torch.full((128,), float("nan"), device="cuda",
+                        dtype=torch.float32 if dw_fp32 else torch.bfloat16)
+        _, _, dw = binding.gated_rmsnorm_bwd(x, x, w, x, EPS, dw_fp32=dw_fp32, dw=dw)
+        torch.cuda.synchronize()
+        assert torch.all(dw == 0).item()
+
+
+def _special_inputs():
+    """Rows that exercise the degenerate cases of the operator."""
+    rows = 64
+    inp = make_inputs(rows, seed=7, device="cpu")
+    x = inp["x"].float()
+    g = inp["g"].float()
+    x[0] = 0.0                      # all-zero row: r = eps^-1/2, y = 0
+    x[1] = 3.0                      # constant row
+    x[2] = -0.5
+    g[3] = 0.0                      # gate zero: y = 0, dg = dy w n / 2
+    g[4] = 80.0                     # sigmoid saturates at 1: silu = g
+    g[5] = -1000.0                  # sigmoid underflows to 0: y, dx, dg = 0
+    g[12] = -80.0                   # sigmoid(-80) ~ 1.8e-35: tiny but not zero
+    g[6, ::2] = 1e4
+    g[6, 1::2] = -1e4
+    x[7] *= 100.0                   # outlier row
+    x[8] *= 1e-15                   # tiny row: eps dominates when eps > 0
+    x[9, 1:] = 0.0                  # a single non-zero entry
+    x[10] *= 1e15                   # large row (mean square 1e30, still FP32)
+    x[11, :64] = 0.0                # half of the row zero
+    inp["x"] = x.to(torch.bfloat16)
+    inp["g"] = g.to(torch.bfloat16)
+    return {k: v.cuda() for k, v in inp.items()}
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1.0, 0.0])
+def test_special_values(eps):
+    say(f"[parity] special values eps={eps}")
+    inp = _special_inputs()
+    if eps == 0.0:  # a zero row has no norm without eps; drop it
+        inp["x"][0] = 1.0
+    y_ref, dx_ref, dg_ref, dw_ref = oracle_all(inp, eps)
+    for dw_fp32 in (True, False):
+        y, dx, dg, dw = gpu_all(inp, eps, dw_fp32)
+        assert_acts_close("y", y, y_ref)
+        assert_acts_close("dx", dx, dx_ref)
+        assert_acts_close("dg", dg, dg_ref)
+        assert_dw_close(dw, dw_ref, dw_fp32)
+        yf, dxf, dgf = f64(y), f64(dx), f64(dg)
+        assert np.all(yf[3] == 0.0)
+        assert np.all(yf[5] == 0.0) and np.all(dxf[5] == 0.0) and np.all(dgf[5] == 0.0)
+        if eps > 0:
+            assert np.all(yf[0] == 0.0)
+
+
+def test_every_output_element_written():
+    """Outputs pre-filled with NaN: after the call no NaN is left."""
+    rows = 1037
+    say(f"[parity] NaN-poisoned outputs rows={rows}")
+    inp = make_inputs(rows, seed=11, device="cuda")
+    nan = lambda: torch.full((rows, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y, dx, dg = nan(), nan(), nan()
+    dw = torch.full((128,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((binding.gated_rmsnorm_workspace_bytes(rows) // 4,), float("nan"),
+                    device="cuda")
+    binding.gated_rmsnorm_workspace_init(ws)
+    binding.gated_rmsnorm_ckpt_step(inp["x"], inp["g"], inp["w"], inp["dy"], EPS, True,
+                                    y=y, dx=dx, dg=dg, dw=dw, workspace=ws)
+    torch.cuda.synchronize()
+    for t in (y, dx, dg, dw):
+        assert not torch.isnan(t).any().item()
+
+
+def test_adjacent_buffers_accepted():
+    """Inputs and outputs packed back to back in one allocation (no overlap)."""
+    rows = 300
+    say(f"[parity] adjacent slices rows={rows}")
+    inp = make_inputs(rows, seed=12, device="cuda")
+    big = torch.empty(6 * rows, 128, dtype=torch.bfloat16, device="cuda")
+    x, g, dy, y, dx, dg = (big[k * rows:(k + 1) * rows] for k in range(6))
+    x.copy_(inp["x"]); g.copy_(inp["g"]); dy.copy_(inp["dy"])
+    binding.gated_rmsnorm_fwd(x, g, inp["w"], EPS, y=y)
+    _, _, dw = binding.gated_rmsnorm_bwd(x, g, inp["w"], dy, EPS, True, dx=dx, dg=dg)
+    torch.cuda.synchronize()
+    y_ref, dx_ref, dg_ref, dw_ref = oracle_all(inp, EPS)
+    assert_acts_close("y", y, y_ref)
+    assert_acts_close("dx", dx, dx_ref)
+    assert_acts_close("dg", dg, dg_ref)
+    assert_dw_close(dw, dw_ref, True)
+
+
+def test_inplace_dx_rejected():
+    inp = make_inputs(64, seed=13, device="cuda")
+    with pytest.raises(binding.GatedRMSNormError, match="ALIAS"):
+        binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], EPS,
+                                  dx=inp["x"])
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times.
+
+def _sample_rows(rows, extra=None, seed=0):
+    rng = np.random.default_rng(seed)
+    idx = np.concatenate([np.arange(min(512, rows)),
+                          np.arange(max(0, rows - 513), rows),
+                          rng.integers(0, rows, 2048)])
+    if extra is not None:
+        idx = np.concatenate([idx, extra])
+    return np.unique(idx)
+
+
+def _oracle_dw_streamed(inp, eps, chunk=1 << 20):
+    """Oracle dw over every row, in row chunks whose FP64 sums are added in order."""
+    rows = inp["x"].shape[0]
+    w = bits(inp["w"])
+    dw = np.zeros(128)
+    for r0 in range(0, rows, chunk):
+        sl = slice(r0, min(rows, r0 + chunk))
+        _, _, part = oracle.bwd(bits(inp["x"][sl]), bits(inp["g"][sl]), w,
+                                bits(inp["dy"][sl]), eps)
+        dw += part
+    return dw
+
+
+@pytest.mark.parametrize("name", ["7684x48", "32768x48", "65536x48", "262144x48_outliers"])
+def test_full_size_sampled(name):
+    wl = WORKLOADS[name]
+    say(f"[parity] {name} rows={wl.rows} full size, sampled rows")
+    inp = make_workload_inputs(wl, device="cuda")
+    y, dx, dg, dw32 = gpu_all(inp, wl.eps, True)
+    extra = None
+    if wl.outlier_frac > 0:
+        big = (inp["x"].float().abs().amax(dim=1) > 20).nonzero().flatten()
+        assert big.numel() >= int(wl.rows * wl.outlier_frac) * 0.99
+        extra = big[:512].cpu().numpy()
+    idx_np = _sample_rows(wl.rows, extra)
+    idx = torch.from_numpy(idx_np).cuda()
+    sub = {k: (v[idx] if k != "w" else v) for k, v in inp.items()}
+    y_ref, dx_ref, dg_ref, _ = oracle_all(sub, wl.eps, want_dw=False)
+    assert_acts_close("y", y[idx], y_ref)
+    assert_acts_close("dx", dx[idx], dx_ref)
+    assert_acts_close("dg", dg[idx], dg_ref)
+    dw_ref = _oracle_dw_streamed(inp, wl.eps)
+    e32 = assert_dw_close(dw32, dw_ref, True)
+    _, _, dw16 = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], wl.eps,
+                                           dw_fp32=False)
+    torch.cuda.synchronize()
+    u16 = assert_dw_close(dw16, dw_ref, False)
+    say(f"  dw fp32 rel err {e32:.2e}, dw bf16 worst {u16} ulp")
