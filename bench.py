@@ -72,6 +72,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time of the oracle baseline")
+    p.add_argument("--profile-op", choices=("fwd", "bwd", "ckpt"),
+                   help="profiling mode: run only this operation (warmup, then "
+                        "--op-reps launches in buffer rotation) and print its timing; "
+                        "the profiler's per-kernel average then covers exactly these "
+                        "launches")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files "
                         "(FETCH_SIZE, WRITE_SIZE) of this benchmark into the per-launch "
@@ -174,6 +179,19 @@ def main():
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / reps
+
+    if args.profile_op:
+        fn, nbytes = {"fwd": (op_fwd, fwd_bytes), "bwd": (op_bwd, bwd_bytes),
+                      "ckpt": (op_ckpt, ckpt_bytes)}[args.profile_op]
+        for i in range(args.warmup):
+            fn(sets[i % nsets])
+        us = rotate_time(fn, args.op_reps)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"profile_op": args.profile_op, "workload": wl.name,
+                          "launches": args.op_reps, "avg_us_events": round(us, 3),
+                          "GB/s": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}),
+              flush=True)
+        return
 
     # ---- the contract measurement: K timed steps --------------------------
     for i in range(args.warmup):
