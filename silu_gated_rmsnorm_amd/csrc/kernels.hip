@@ -42,7 +42,10 @@
 #define GRN_BWD_MIN_WAVES 0  // >0: ask for at least this many waves per SIMD
 #endif
 #ifndef GRN_BWD_PREFETCH
-#define GRN_BWD_PREFETCH 1   // 1: load the next step while computing this one
+#define GRN_BWD_PREFETCH 1   // steps of loads kept in flight ahead of the one
+#endif                       // being computed (0 = none)
+#ifndef GRN_SUM_BATCH
+#define GRN_SUM_BATCH 8      // partial rows per thread per round trip in the dw tree
 #endif
 #ifndef GRN_BWD_WG_PER_CU
 #define GRN_BWD_WG_PER_CU -1 // backward grid cap per CU; 0 = occupancy limit,
@@ -266,30 +269,28 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
     const int64_t left = rows - row_of(it);
     return (int)(left < 0 ? 0 : (left > kStepRows ? kStepRows : left));
   };
-  BwdRaw<U> cur, nxt;
-  {
-    const int64_t base = row_of(0) * kLanesPerRow;
-    bwd_load<U, kFull>(cur, x + base, g + base, dy + base, lane, nvalid_of(0));
+  // A ring of kDepth register buffers: step it+kDepth-1 is loaded while
+  // step it is computed.
+  constexpr int kDepth = GRN_BWD_PREFETCH + 1;
+  BwdRaw<U> buf[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth - 1; ++k) {
+    if (k < kIters) {
+      const int64_t base = row_of(k) * kLanesPerRow;
+      bwd_load<U, kFull>(buf[k], x + base, g + base, dy + base, lane, nvalid_of(k));
+    }
   }
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
-    if (GRN_BWD_PREFETCH && it + 1 < kIters) {
-      const int64_t base = row_of(it + 1) * kLanesPerRow;
-      bwd_load<U, kFull>(nxt, x + base, g + base, dy + base, lane,
-                         nvalid_of(it + 1));
+    const int ahead = it + kDepth - 1;
+    if (ahead < kIters) {
+      const int64_t base = row_of(ahead) * kLanesPerRow;
+      bwd_load<U, kFull>(buf[ahead % kDepth], x + base, g + base, dy + base, lane,
+                         nvalid_of(ahead));
     }
     const int64_t base = row_of(it) * kLanesPerRow;
-    bwd_compute<U, kFull>(cur, dx + base, dg + base, wf, eps, lane,
+    bwd_compute<U, kFull>(buf[it % kDepth], dx + base, dg + base, wf, eps, lane,
                           nvalid_of(it), acc);
-    if (it + 1 < kIters) {
-      if (GRN_BWD_PREFETCH) {
-        cur = nxt;
-      } else {
-        const int64_t nbase = row_of(it + 1) * kLanesPerRow;
-        bwd_load<U, kFull>(cur, x + nbase, g + nbase, dy + nbase, lane,
-                           nvalid_of(it + 1));
-      }
-    }
   }
 }
 
@@ -328,8 +329,8 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // Column sums of a [count, 128] FP32 array, in a fixed order.  Thread t of
 // the workgroup owns columns 4*(t%32) .. 4*(t%32)+3 and row slot t/32: it
 // adds rows slot, slot+S, slot+2S, ... (S = threads/32 slots) in increasing
-// order (16-byte loads issued eight rows at a time; rows past the end read
-// as zero).
+// order (16-byte loads issued GRN_SUM_BATCH rows at a time, so one round
+// trip covers up to 8 * GRN_SUM_BATCH rows; rows past the end read as zero).
 // The S slots of each column are then added in slot order.  The result is
 // valid in threads 0..127 (one column each).
 template <int kThreads>
@@ -337,7 +338,7 @@ __device__ __forceinline__ float column_sum_fixed(const float* __restrict__ src,
                                                   int64_t count,
                                                   float* __restrict__ lds) {
   constexpr int kSlots = kThreads / 32;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = GRN_SUM_BATCH;
   const int t = threadIdx.x;
   const int quad = t & 31;
   const int slot = t / 32;
