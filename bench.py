@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="7684x48")
+    p.add_argument("--layout", choices=("packed", "fused"), default="packed",
+                   help="packed rows, or x|g and dx|dg as the two halves of fused "
+                        "[rows, 256] buffers (row stride 256)")
     p.add_argument("--op-reps", type=int, default=50,
                    help="launches per operation in the per-op timings")
     p.add_argument("--no-ops", action="store_true", help="skip per-op timings")
@@ -117,12 +120,19 @@ def main():
 
     inp = make_workload_inputs(wl, device=dev)
     ws_bytes = binding.gated_rmsnorm_workspace_bytes(rows)
+    fused = args.layout == "fused"
     sets = []
     for _ in range(nsets):
-        st = {k: inp[k].clone() for k in ("x", "g", "dy")}
+        if fused:
+            proj = torch.cat([inp["x"], inp["g"]], dim=1)
+            dproj = torch.empty_like(proj)
+            st = {"x": proj[:, :D], "g": proj[:, D:], "dy": inp["dy"].clone(),
+                  "dx": dproj[:, :D], "dg": dproj[:, D:], "y": torch.empty_like(inp["x"])}
+        else:
+            st = {k: inp[k].clone() for k in ("x", "g", "dy")}
+            for k in ("y", "dx", "dg"):
+                st[k] = torch.empty_like(inp["x"])
         st["w"] = inp["w"]
-        for k in ("y", "dx", "dg"):
-            st[k] = torch.empty_like(inp["x"])
         st["dw16"] = torch.empty(D, dtype=torch.bfloat16, device=dev)
         st["dw32"] = torch.empty(D, dtype=torch.float32, device=dev)
         st["ws"] = binding.new_workspace(rows, dev)
@@ -137,22 +147,41 @@ def main():
             raise RuntimeError(lib.gated_rmsnorm_status_string(status).decode())
 
     # Raw C-ABI calls on buffer set `st` (no per-call Python checks).
+    R_ = lambda t: t.stride(0)  # noqa: E731  (row stride, elements)
+
     def op_fwd(st):
-        check(lib.gated_rmsnorm_fwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["y"]), rows, D,
-                                    eps, 0, S()))
+        if fused:
+            check(lib.gated_rmsnorm_fwd_strided(P(st["x"]), R_(st["x"]), P(st["g"]),
+                                                R_(st["g"]), P(st["w"]), P(st["y"]),
+                                                R_(st["y"]), rows, D, eps, 0, S()))
+        else:
+            check(lib.gated_rmsnorm_fwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["y"]), rows,
+                                        D, eps, 0, S()))
 
     def op_bwd(st, fp32=False):
         dw = st["dw32"] if fp32 else st["dw16"]
-        check(lib.gated_rmsnorm_bwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
-                                    P(st["dx"]), P(st["dg"]), P(dw), P(st["ws"]), ws_bytes,
-                                    rows, D, eps, 0, int(fp32), S()))
+        if fused:
+            check(lib.gated_rmsnorm_bwd_strided(
+                P(st["x"]), R_(st["x"]), P(st["g"]), R_(st["g"]), P(st["w"]), P(st["dy"]),
+                R_(st["dy"]), P(st["dx"]), R_(st["dx"]), P(st["dg"]), R_(st["dg"]), P(dw),
+                P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), S()))
+        else:
+            check(lib.gated_rmsnorm_bwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
+                                        P(st["dx"]), P(st["dg"]), P(dw), P(st["ws"]),
+                                        ws_bytes, rows, D, eps, 0, int(fp32), S()))
 
     def op_ckpt(st, fp32=False):
         dw = st["dw32"] if fp32 else st["dw16"]
-        check(lib.gated_rmsnorm_ckpt_step(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
-                                          P(st["y"]), P(st["dx"]), P(st["dg"]), P(dw),
-                                          P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32),
-                                          S()))
+        if fused:
+            check(lib.gated_rmsnorm_ckpt_step_strided(
+                P(st["x"]), R_(st["x"]), P(st["g"]), R_(st["g"]), P(st["w"]), P(st["dy"]),
+                R_(st["dy"]), P(st["y"]), R_(st["y"]), P(st["dx"]), R_(st["dx"]), P(st["dg"]),
+                R_(st["dg"]), P(dw), P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), S()))
+        else:
+            check(lib.gated_rmsnorm_ckpt_step(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
+                                              P(st["y"]), P(st["dx"]), P(st["dg"]), P(dw),
+                                              P(st["ws"]), ws_bytes, rows, D, eps, 0,
+                                              int(fp32), S()))
 
     def op_step(st):
         op_fwd(st)
@@ -188,6 +217,7 @@ def main():
         us = rotate_time(fn, args.op_reps)
         gbps = nbytes / (us * 1e-6) / 1e9
         print(json.dumps({"profile_op": args.profile_op, "workload": wl.name,
+                          "layout": args.layout,
                           "launches": args.op_reps, "avg_us_events": round(us, 3),
                           "GB/s": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}),
               flush=True)
@@ -248,6 +278,31 @@ def main():
             rec(name, rotate_time(lambda st: by_set[id(st)].replay(), R), nbytes)
             del graphs, by_set
 
+        # Batched: N launches (rotating over the sets) captured into one HIP
+        # graph and replayed once, so the host's launch overhead drops out;
+        # what remains is back-to-back GPU time per launch.  This is the
+        # figure that matters for small workloads whose kernels take about
+        # as long as the host needs to enqueue one.
+        nb = max(2 * nsets, 20)
+        for name, (fn, nbytes) in (("fwd_batched", (op_fwd, fwd_bytes)),
+                                   ("bwd_batched", (op_bwd, bwd_bytes)),
+                                   ("step_batched", (op_step, step_bytes)),
+                                   ("ckpt_batched", (op_ckpt, ckpt_bytes))):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s):
+                for i in range(nb):
+                    fn(sets[i % nsets])
+            gr.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            rec(name, a.elapsed_time(b) * 1e3 / nb, nbytes)
+            del gr
+
         # Same buffers every launch (no rotation): inputs partly served by the
         # Infinity Cache; reported for contrast only.
         one = sets[0]
@@ -294,6 +349,7 @@ def main():
         "io_dtype": "bf16",
         "data": "synthetic (seeded normal BF16 inputs resident in HBM)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "rows": rows, "D": D,
+                   "layout": args.layout,
                    "eps": eps, "step": "fwd + bwd (deterministic BF16 dw)",
                    "bytes_per_step": step_bytes, "buffer_sets": nsets},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -25,7 +25,12 @@
  * Conventions for every entry point
  * ---------------------------------
  *  - Layout: every activation (x, g, dy, y, dx, dg) is a row-major
- *    [rows, D] array with rows packed (row stride = D elements).  w is [D].
+ *    [rows, D] array.  The plain entry points take packed rows (row stride
+ *    = D elements); the _strided ones take a row stride per activation, in
+ *    elements: D <= stride <= 2^24 and a multiple of 8 (16-byte rows), e.g.
+ *    x and g as the two halves of a fused [rows, 2D] projection, which the
+ *    commit 10c6017 message of flashinfer PR #8701 distinguishes from rows
+ *    held packed.  w is [D].
  *  - dtype: GRN_DTYPE_BF16 is the only accepted element type.  Arithmetic is
  *    FP32; each BF16 output is rounded once, to nearest even.
  *  - D: only D = 128 is accepted (one row = 256 bytes).
@@ -40,7 +45,9 @@
  *  - Alignment: activations, w and the workspace must be 16-byte aligned;
  *    dw 4-byte aligned (FP32) or 2-byte aligned (BF16).
  *  - Aliasing: no output may overlap any input, another output or the
- *    workspace.  An in-place dx = x would let one workgroup overwrite rows
+ *    workspace.  Rows of equal stride that interleave without sharing a
+ *    byte (dx and dg as the two halves of one fused buffer) do not overlap;
+ *    for unequal strides the check is on address ranges (conservative).  An in-place dx = x would let one workgroup overwrite rows
  *    that another has not read yet; the review of flashinfer PR #8878
  *    ("Follow-up" findings) reports that race for a sibling kernel.
  *  - eps: finite and >= 0.
@@ -66,9 +73,11 @@ extern "C" {
 typedef enum grn_status {
     GRN_OK = 0,
     GRN_ERR_NULL = 1,      /* a required pointer is NULL                     */
-    GRN_ERR_SHAPE = 2,     /* D != 128, rows < 0 or rows > GRN_MAX_ROWS      */
+    GRN_ERR_SHAPE = 2,     /* D != 128, rows outside [0, GRN_MAX_ROWS], or
+                              a row stride outside [D, 2^24]                 */
     GRN_ERR_DTYPE = 3,     /* dtype is not BF16, or dw_fp32 is not 0 or 1    */
-    GRN_ERR_ALIGN = 4,     /* a pointer is not aligned as required           */
+    GRN_ERR_ALIGN = 4,     /* a pointer, or a row stride, is not aligned as
+                              required                                       */
     GRN_ERR_ALIAS = 5,     /* an output overlaps an input, output or ws      */
     GRN_ERR_WORKSPACE = 6, /* workspace missing or smaller than required     */
     GRN_ERR_EPS = 7,       /* eps is negative, infinite or NaN               */
@@ -81,7 +90,7 @@ enum { GRN_DTYPE_BF16 = 0 };
 
 /* Bytes of device workspace the backward needs for `rows` rows of width D:
  * a fixed region of arrival counters, one FP32 partial dw of D values per
- * chunk of gated_rmsnorm_chunk_rows() rows, and one per group of about
+ * chunk of gated_rmsnorm_chunk_rows(rows) rows, and one per group of about
  * sqrt(chunks) chunks.  Returns 0 for rows <= 0 or an unsupported D.
  *
  * Workspace contract: the counter region must be zero before the first
@@ -92,8 +101,10 @@ enum { GRN_DTYPE_BF16 = 0 };
  * not share a workspace. */
 size_t gated_rmsnorm_workspace_bytes(int64_t rows, int32_t D);
 
-/* Number of rows in one dw chunk: rows [c*R, (c+1)*R) form chunk c. */
-int32_t gated_rmsnorm_chunk_rows(void);
+/* Rows R in one dw chunk of a backward over `rows` rows: rows [c*R, (c+1)*R)
+ * form chunk c.  R depends only on `rows` (it is 128 for every rows > 0 in
+ * this version); 0 for rows <= 0. */
+int32_t gated_rmsnorm_chunk_rows(int64_t rows);
 
 /* Forward: y = x * rsqrt(mean(x^2) + eps) * w * silu(g), row by row.
  * In:  x, g [rows, D] BF16; w [D] BF16.   Out: y [rows, D] BF16.
@@ -134,6 +145,34 @@ grn_status gated_rmsnorm_ckpt_step(const void *x, const void *g,
                                    int64_t rows, int32_t D, float eps,
                                    int32_t dtype, int32_t dw_fp32,
                                    void *stream);
+
+/* Strided forms.  Same as the plain entry points, with each activation's
+ * row stride in elements (see Layout above).  Invalid strides:
+ * stride < D or > 2^24 -> GRN_ERR_SHAPE; not a multiple of 8 -> GRN_ERR_ALIGN.
+ * Results are bitwise those of the plain entry points on packed copies. */
+grn_status gated_rmsnorm_fwd_strided(const void *x, int64_t x_stride,
+                                     const void *g, int64_t g_stride,
+                                     const void *w, void *y, int64_t y_stride,
+                                     int64_t rows, int32_t D, float eps,
+                                     int32_t dtype, void *stream);
+
+grn_status gated_rmsnorm_bwd_strided(const void *x, int64_t x_stride,
+                                     const void *g, int64_t g_stride,
+                                     const void *w, const void *dy,
+                                     int64_t dy_stride, void *dx,
+                                     int64_t dx_stride, void *dg,
+                                     int64_t dg_stride, void *dw,
+                                     void *workspace, size_t workspace_bytes,
+                                     int64_t rows, int32_t D, float eps,
+                                     int32_t dtype, int32_t dw_fp32,
+                                     void *stream);
+
+grn_status gated_rmsnorm_ckpt_step_strided(
+    const void *x, int64_t x_stride, const void *g, int64_t g_stride,
+    const void *w, const void *dy, int64_t dy_stride, void *y, int64_t y_stride,
+    void *dx, int64_t dx_stride, void *dg, int64_t dg_stride, void *dw,
+    void *workspace, size_t workspace_bytes, int64_t rows, int32_t D,
+    float eps, int32_t dtype, int32_t dw_fp32, void *stream);
 
 /* Zero the arrival counters at the front of a workspace (the first
  * gated_rmsnorm_workspace_init_bytes() bytes) by enqueueing a small kernel

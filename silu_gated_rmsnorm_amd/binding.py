@@ -35,9 +35,10 @@ def library_path() -> pathlib.Path:
 
 # Every symbol the header declares, with its ctypes signature.
 _VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
 _SIGS = {
     "gated_rmsnorm_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
-    "gated_rmsnorm_chunk_rows": (ctypes.c_int32, []),
+    "gated_rmsnorm_chunk_rows": (ctypes.c_int32, [ctypes.c_int64]),
     "gated_rmsnorm_fwd": (ctypes.c_int32, [_VP, _VP, _VP, _VP, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_float,
                                             ctypes.c_int32, _VP]),
@@ -50,6 +51,20 @@ _SIGS = {
                                                   ctypes.c_int64, ctypes.c_int32,
                                                   ctypes.c_float, ctypes.c_int32,
                                                   ctypes.c_int32, _VP]),
+    "gated_rmsnorm_fwd_strided": (ctypes.c_int32, [_VP, _I64, _VP, _I64, _VP, _VP, _I64,
+                                                    _I64, ctypes.c_int32, ctypes.c_float,
+                                                    ctypes.c_int32, _VP]),
+    "gated_rmsnorm_bwd_strided": (ctypes.c_int32, [_VP, _I64, _VP, _I64, _VP, _VP, _I64,
+                                                    _VP, _I64, _VP, _I64, _VP, _VP,
+                                                    ctypes.c_size_t, _I64, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.c_int32,
+                                                    ctypes.c_int32, _VP]),
+    "gated_rmsnorm_ckpt_step_strided": (ctypes.c_int32, [_VP, _I64, _VP, _I64, _VP, _VP,
+                                                          _I64, _VP, _I64, _VP, _I64, _VP,
+                                                          _I64, _VP, _VP, ctypes.c_size_t,
+                                                          _I64, ctypes.c_int32,
+                                                          ctypes.c_float, ctypes.c_int32,
+                                                          ctypes.c_int32, _VP]),
     "gated_rmsnorm_workspace_init": (ctypes.c_int32, [_VP, ctypes.c_size_t, _VP]),
     "gated_rmsnorm_workspace_init_bytes": (ctypes.c_size_t, []),
     "gated_rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -87,18 +102,23 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _act(name: str, t: torch.Tensor, rows=None) -> int:
+def _act(name: str, t: torch.Tensor, rows=None):
+    """(pointer, row stride in elements) of a [rows, D] BF16 activation.
+
+    Rows may be strided (a column slice of a wider buffer, e.g. one half of a
+    fused projection) as long as the elements of a row are contiguous."""
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name}: expected a GPU tensor")
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name}: expected bfloat16, got {t.dtype}")
     if t.dim() != 2 or t.shape[1] != D_SUPPORTED:
         raise ValueError(f"{name}: expected shape [rows, {D_SUPPORTED}], got {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name}: rows must be packed (contiguous)")
     if rows is not None and t.shape[0] != rows:
         raise ValueError(f"{name}: expected {rows} rows, got {t.shape[0]}")
-    return t.data_ptr()
+    if t.stride(1) != 1:
+        raise ValueError(f"{name}: the elements of a row must be contiguous")
+    stride = t.stride(0) if t.shape[0] > 1 else D_SUPPORTED
+    return t.data_ptr(), stride
 
 
 def _weight(w: torch.Tensor) -> int:
@@ -114,11 +134,11 @@ def gated_rmsnorm_workspace_bytes(rows: int, D: int = D_SUPPORTED) -> int:
 
 
 def new_workspace(rows: int, device) -> torch.Tensor:
-    """A zero-filled workspace for the backward of `rows` rows (or fewer).
+    """A zero-filled workspace for the backward of `rows` rows.
 
     Its arrival counters start at zero and every backward leaves them at
-    zero, so one workspace can be reused by later calls of any size up to
-    `rows`."""
+    zero, so the workspace can be reused by any later call whose
+    gated_rmsnorm_workspace_bytes() it covers."""
     need = max(gated_rmsnorm_workspace_bytes(rows), 16)
     return torch.zeros(need, dtype=torch.uint8, device=device)
 
@@ -144,12 +164,17 @@ def gated_rmsnorm_fwd(x, g, w, eps: float = 1e-6, y=None):
     """y = x * rsqrt(mean(x^2) + eps) * w * silu(g) row by row; returns y."""
     lib = load_library()
     rows = x.shape[0]
-    px, pg, pw = _act("x", x), _act("g", g, rows), _weight(w)
+    (px, sx), (pg, sg), pw = _act("x", x), _act("g", g, rows), _weight(w)
     if y is None:
-        y = torch.empty_like(x)
-    py = _act("y", y, rows)
-    _check(lib.gated_rmsnorm_fwd(px, pg, pw, py, rows, D_SUPPORTED, float(eps),
-                                 GRN_DTYPE_BF16, _stream(x)))
+        y = torch.empty(rows, D_SUPPORTED, dtype=torch.bfloat16, device=x.device)
+    py, sy = _act("y", y, rows)
+    if sx == sg == sy == D_SUPPORTED:
+        st = lib.gated_rmsnorm_fwd(px, pg, pw, py, rows, D_SUPPORTED, float(eps),
+                                   GRN_DTYPE_BF16, _stream(x))
+    else:
+        st = lib.gated_rmsnorm_fwd_strided(px, sx, pg, sg, pw, py, sy, rows, D_SUPPORTED,
+                                           float(eps), GRN_DTYPE_BF16, _stream(x))
+    _check(st)
     return y
 
 
@@ -158,18 +183,23 @@ def gated_rmsnorm_bwd(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
     """Gradients of sum(dy * y): returns (dx, dg, dw); dw is FP32 if dw_fp32."""
     lib = load_library()
     rows = x.shape[0]
-    px, pg, pw, pdy = _act("x", x), _act("g", g, rows), _weight(w), _act("dy", dy, rows)
-    dx = torch.empty_like(x) if dx is None else dx
-    dg = torch.empty_like(x) if dg is None else dg
-    dw_dtype = torch.float32 if dw_fp32 else torch.bfloat16
-    dw = torch.empty(D_SUPPORTED, dtype=dw_dtype, device=x.device) if dw is None else dw
-    if dw.dtype != dw_dtype or dw.shape != (D_SUPPORTED,) or dw.device != x.device:
-        raise ValueError(f"dw: expected a {dw_dtype} [{D_SUPPORTED}] tensor on the inputs' device")
+    (px, sx), (pg, sg), pw = _act("x", x), _act("g", g, rows), _weight(w)
+    pdy, sdy = _act("dy", dy, rows)
+    dx = _new_act(x) if dx is None else dx
+    dg = _new_act(x) if dg is None else dg
+    (pdx, sdx), (pdg, sdg) = _act("dx", dx, rows), _act("dg", dg, rows)
+    dw = _dw(dw, dw_fp32, x.device)
     ws, ws_bytes = _workspace(rows, x.device, workspace)
-    _check(lib.gated_rmsnorm_bwd(px, pg, pw, pdy, _act("dx", dx, rows), _act("dg", dg, rows),
-                                 dw.data_ptr(), ws.data_ptr(), ws_bytes, rows,
-                                 D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
-                                 int(bool(dw_fp32)), _stream(x)))
+    if sx == sg == sdy == sdx == sdg == D_SUPPORTED:
+        st = lib.gated_rmsnorm_bwd(px, pg, pw, pdy, pdx, pdg, dw.data_ptr(), ws.data_ptr(),
+                                   ws_bytes, rows, D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
+                                   int(bool(dw_fp32)), _stream(x))
+    else:
+        st = lib.gated_rmsnorm_bwd_strided(px, sx, pg, sg, pw, pdy, sdy, pdx, sdx, pdg, sdg,
+                                           dw.data_ptr(), ws.data_ptr(), ws_bytes, rows,
+                                           D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
+                                           int(bool(dw_fp32)), _stream(x))
+    _check(st)
     return dx, dg, dw
 
 
@@ -178,18 +208,38 @@ def gated_rmsnorm_ckpt_step(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = Fals
     """Forward, recomputed forward, backward: returns (y, dx, dg, dw)."""
     lib = load_library()
     rows = x.shape[0]
-    px, pg, pw, pdy = _act("x", x), _act("g", g, rows), _weight(w), _act("dy", dy, rows)
-    y = torch.empty_like(x) if y is None else y
-    dx = torch.empty_like(x) if dx is None else dx
-    dg = torch.empty_like(x) if dg is None else dg
-    dw_dtype = torch.float32 if dw_fp32 else torch.bfloat16
-    dw = torch.empty(D_SUPPORTED, dtype=dw_dtype, device=x.device) if dw is None else dw
-    if dw.dtype != dw_dtype or dw.shape != (D_SUPPORTED,) or dw.device != x.device:
-        raise ValueError(f"dw: expected a {dw_dtype} [{D_SUPPORTED}] tensor on the inputs' device")
+    (px, sx), (pg, sg), pw = _act("x", x), _act("g", g, rows), _weight(w)
+    pdy, sdy = _act("dy", dy, rows)
+    y = _new_act(x) if y is None else y
+    dx = _new_act(x) if dx is None else dx
+    dg = _new_act(x) if dg is None else dg
+    (py, sy), (pdx, sdx), (pdg, sdg) = (_act("y", y, rows), _act("dx", dx, rows),
+                                        _act("dg", dg, rows))
+    dw = _dw(dw, dw_fp32, x.device)
     ws, ws_bytes = _workspace(rows, x.device, workspace)
-    _check(lib.gated_rmsnorm_ckpt_step(px, pg, pw, pdy, _act("y", y, rows),
-                                       _act("dx", dx, rows), _act("dg", dg, rows),
-                                       dw.data_ptr(), ws.data_ptr(), ws_bytes, rows,
-                                       D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
-                                       int(bool(dw_fp32)), _stream(x)))
+    if sx == sg == sdy == sy == sdx == sdg == D_SUPPORTED:
+        st = lib.gated_rmsnorm_ckpt_step(px, pg, pw, pdy, py, pdx, pdg, dw.data_ptr(),
+                                         ws.data_ptr(), ws_bytes, rows, D_SUPPORTED,
+                                         float(eps), GRN_DTYPE_BF16, int(bool(dw_fp32)),
+                                         _stream(x))
+    else:
+        st = lib.gated_rmsnorm_ckpt_step_strided(px, sx, pg, sg, pw, pdy, sdy, py, sy, pdx,
+                                                 sdx, pdg, sdg, dw.data_ptr(), ws.data_ptr(),
+                                                 ws_bytes, rows, D_SUPPORTED, float(eps),
+                                                 GRN_DTYPE_BF16, int(bool(dw_fp32)),
+                                                 _stream(x))
+    _check(st)
     return y, dx, dg, dw
+
+
+def _new_act(like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(like.shape[0], D_SUPPORTED, dtype=torch.bfloat16, device=like.device)
+
+
+def _dw(dw, dw_fp32, device):
+    dw_dtype = torch.float32 if dw_fp32 else torch.bfloat16
+    if dw is None:
+        return torch.empty(D_SUPPORTED, dtype=dw_dtype, device=device)
+    if dw.dtype != dw_dtype or dw.shape != (D_SUPPORTED,) or dw.device != device:
+        raise ValueError(f"dw: expected a {dw_dtype} [{D_SUPPORTED}] tensor on the inputs' device")
+    return dw

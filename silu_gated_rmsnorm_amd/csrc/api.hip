@@ -11,16 +11,39 @@ namespace {
 constexpr int32_t kSupportedD = 128;
 constexpr size_t kRowBytes = kSupportedD * 2;  // one BF16 row
 
-struct Range {
+// A set of `rows` rows of `width` bytes, `pitch` bytes apart, from `p`.
+struct Rows {
   const void* p;
-  size_t n;
+  int64_t rows;
+  int64_t pitch;
+  int64_t width;
 };
 
-bool overlap(Range a, Range b) {
-  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+uintptr_t extent(const Rows& a) {
+  return a.rows <= 0 ? 0 : (uintptr_t)((a.rows - 1) * a.pitch + a.width);
+}
+
+// True if two row sets share a byte.  Exact when the pitches are equal
+// (rows interleaved in one buffer, e.g. two halves of a fused projection, do
+// not overlap); conservative (address ranges) otherwise.
+bool overlap(const Rows& a, const Rows& b) {
+  const uintptr_t ea = extent(a), eb = extent(b);
+  if (a.p == nullptr || b.p == nullptr || ea == 0 || eb == 0) return false;
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a.p);
   const uintptr_t pb = reinterpret_cast<uintptr_t>(b.p);
-  return pa < pb + b.n && pb < pa + a.n;
+  if (!(pa < pb + eb && pb < pa + ea)) return false;
+  if (a.pitch != b.pitch || a.rows <= 1 || b.rows <= 1) return true;
+  const uintptr_t pitch = (uintptr_t)a.pitch;
+  const uintptr_t lo = pa < pb ? pa : pb;
+  const uintptr_t delta = ((pa < pb ? pb : pa) - lo) % pitch;
+  const uintptr_t w_lo = (pa < pb ? a.width : b.width);   // row width at lo
+  const uintptr_t w_hi = (pa < pb ? b.width : a.width);
+  // rows of the later set start `delta` bytes into each pitch of the earlier
+  return !(delta >= w_lo && delta + w_hi <= pitch);
+}
+
+Rows plain(const void* p, size_t bytes) {
+  return Rows{p, bytes > 0 ? 1 : 0, (int64_t)bytes, (int64_t)bytes};
 }
 
 bool aligned(const void* p, uintptr_t a) {
@@ -48,39 +71,57 @@ grn_status check_eps(float eps) {
   return GRN_OK;
 }
 
+// A row stride (elements) is at least D, at most kMaxStride, and keeps every
+// row 16-byte aligned.
+grn_status check_stride(int64_t stride) {
+  if (stride < kSupportedD || stride > grn::kMaxStride) return GRN_ERR_SHAPE;
+  if (stride % 8 != 0) return GRN_ERR_ALIGN;
+  return GRN_OK;
+}
+
 size_t workspace_need(int64_t rows) {
   return rows > 0 ? grn::bwd_layout(rows).bytes : 0;
 }
 
+struct Act {
+  const void* p;
+  int64_t stride;  // elements
+};
+
 // Pointer rules shared by every entry point.  `acts` are [rows, D] BF16
 // activations (inputs first, then outputs); `n_in` of them are inputs.
-grn_status check_buffers(int64_t rows, const void* const* acts, int n_acts,
-                         int n_in, const void* w, const void* ws,
-                         size_t ws_need, const void* dw, size_t dw_bytes) {
-  const size_t act_bytes = static_cast<size_t>(rows) * kRowBytes;
+grn_status check_buffers(int64_t rows, const Act* acts, int n_acts, int n_in,
+                         const void* w, const void* ws, size_t ws_need,
+                         const void* dw, size_t dw_bytes) {
   if (w == nullptr) return GRN_ERR_NULL;
   if (rows > 0)
     for (int k = 0; k < n_acts; ++k)
-      if (acts[k] == nullptr) return GRN_ERR_NULL;
+      if (acts[k].p == nullptr) return GRN_ERR_NULL;
   if (dw_bytes > 0 && dw == nullptr) return GRN_ERR_NULL;
   if (ws_need > 0 && ws == nullptr) return GRN_ERR_WORKSPACE;
 
+  for (int k = 0; k < n_acts; ++k) {
+    const grn_status st = check_stride(acts[k].stride);
+    if (st != GRN_OK) return st;
+  }
   if (!aligned(w, 16)) return GRN_ERR_ALIGN;
   for (int k = 0; k < n_acts; ++k)
-    if (!aligned(acts[k], 16)) return GRN_ERR_ALIGN;
+    if (!aligned(acts[k].p, 16)) return GRN_ERR_ALIGN;
   if (ws_need > 0 && !aligned(ws, 16)) return GRN_ERR_ALIGN;
   if (dw_bytes > 0 && !aligned(dw, dw_bytes / kSupportedD)) return GRN_ERR_ALIGN;
 
   // Outputs: activations n_in.., dw, and the workspace (written as scratch).
-  Range outs[8];
+  Rows outs[8];
   int n_out = 0;
-  for (int k = n_in; k < n_acts; ++k) outs[n_out++] = Range{acts[k], act_bytes};
-  if (dw_bytes > 0) outs[n_out++] = Range{dw, dw_bytes};
-  if (ws_need > 0) outs[n_out++] = Range{ws, ws_need};
-  Range ins[8];
+  for (int k = n_in; k < n_acts; ++k)
+    outs[n_out++] = Rows{acts[k].p, rows, acts[k].stride * 2, (int64_t)kRowBytes};
+  if (dw_bytes > 0) outs[n_out++] = plain(dw, dw_bytes);
+  if (ws_need > 0) outs[n_out++] = plain(ws, ws_need);
+  Rows ins[8];
   int n_ins = 0;
-  for (int k = 0; k < n_in; ++k) ins[n_ins++] = Range{acts[k], act_bytes};
-  ins[n_ins++] = Range{w, kRowBytes};
+  for (int k = 0; k < n_in; ++k)
+    ins[n_ins++] = Rows{acts[k].p, rows, acts[k].stride * 2, (int64_t)kRowBytes};
+  ins[n_ins++] = plain(w, kRowBytes);
   for (int a = 0; a < n_out; ++a) {
     for (int b = 0; b < n_ins; ++b)
       if (overlap(outs[a], ins[b])) return GRN_ERR_ALIAS;
@@ -101,20 +142,66 @@ size_t gated_rmsnorm_workspace_bytes(int64_t rows, int32_t D) {
   return workspace_need(rows);
 }
 
-int32_t gated_rmsnorm_chunk_rows(void) { return grn::kChunkRows; }
+int32_t gated_rmsnorm_chunk_rows(int64_t rows) {
+  return rows <= 0 ? 0 : grn::chunk_rows_for(rows);
+}
 
 size_t gated_rmsnorm_workspace_init_bytes(void) { return grn::kCounterBytes; }
+
+grn_status gated_rmsnorm_fwd_strided(const void* x, int64_t x_stride,
+                                     const void* g, int64_t g_stride,
+                                     const void* w, void* y, int64_t y_stride,
+                                     int64_t rows, int32_t D, float eps,
+                                     int32_t dtype, void* stream) {
+  grn_status st = check_common(rows, D, dtype);
+  if (st != GRN_OK) return st;
+  if ((st = check_eps(eps)) != GRN_OK) return st;
+  const Act acts[3] = {{x, x_stride}, {g, g_stride}, {y, y_stride}};
+  st = check_buffers(rows, acts, 3, 2, w, nullptr, 0, nullptr, 0);
+  if (st != GRN_OK) return st;
+  grn::RowStrides rs;
+  rs.x = x_stride;
+  rs.g = g_stride;
+  rs.y = y_stride;
+  return hip_status(grn::launch_fwd(x, g, w, y, rs, rows, eps, env_max_wg(),
+                                    static_cast<hipStream_t>(stream)));
+}
 
 grn_status gated_rmsnorm_fwd(const void* x, const void* g, const void* w,
                              void* y, int64_t rows, int32_t D, float eps,
                              int32_t dtype, void* stream) {
+  return gated_rmsnorm_fwd_strided(x, D, g, D, w, y, D, rows, D, eps, dtype, stream);
+}
+
+grn_status gated_rmsnorm_bwd_strided(const void* x, int64_t x_stride,
+                                     const void* g, int64_t g_stride,
+                                     const void* w, const void* dy,
+                                     int64_t dy_stride, void* dx,
+                                     int64_t dx_stride, void* dg,
+                                     int64_t dg_stride, void* dw,
+                                     void* workspace, size_t workspace_bytes,
+                                     int64_t rows, int32_t D, float eps,
+                                     int32_t dtype, int32_t dw_fp32,
+                                     void* stream) {
   grn_status st = check_common(rows, D, dtype);
   if (st != GRN_OK) return st;
+  if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
   if ((st = check_eps(eps)) != GRN_OK) return st;
-  const void* acts[3] = {x, g, y};
-  st = check_buffers(rows, acts, 3, 2, w, nullptr, 0, nullptr, 0);
+  const size_t need = workspace_need(rows);
+  if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
+  const Act acts[5] = {{x, x_stride}, {g, g_stride}, {dy, dy_stride},
+                       {dx, dx_stride}, {dg, dg_stride}};
+  st = check_buffers(rows, acts, 5, 3, w, workspace, need, dw,
+                     kSupportedD * (dw_fp32 ? 4 : 2));
   if (st != GRN_OK) return st;
-  return hip_status(grn::launch_fwd(x, g, w, y, rows, eps, env_max_wg(),
+  grn::RowStrides rs;
+  rs.x = x_stride;
+  rs.g = g_stride;
+  rs.dy = dy_stride;
+  rs.dx = dx_stride;
+  rs.dg = dg_stride;
+  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, workspace,
+                                    rs, rows, eps, env_max_wg(),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -123,19 +210,43 @@ grn_status gated_rmsnorm_bwd(const void* x, const void* g, const void* w,
                              void* workspace, size_t workspace_bytes,
                              int64_t rows, int32_t D, float eps,
                              int32_t dtype, int32_t dw_fp32, void* stream) {
+  return gated_rmsnorm_bwd_strided(x, D, g, D, w, dy, D, dx, D, dg, D, dw,
+                                   workspace, workspace_bytes, rows, D, eps,
+                                   dtype, dw_fp32, stream);
+}
+
+grn_status gated_rmsnorm_ckpt_step_strided(
+    const void* x, int64_t x_stride, const void* g, int64_t g_stride,
+    const void* w, const void* dy, int64_t dy_stride, void* y, int64_t y_stride,
+    void* dx, int64_t dx_stride, void* dg, int64_t dg_stride, void* dw,
+    void* workspace, size_t workspace_bytes, int64_t rows, int32_t D,
+    float eps, int32_t dtype, int32_t dw_fp32, void* stream) {
   grn_status st = check_common(rows, D, dtype);
   if (st != GRN_OK) return st;
   if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
   if ((st = check_eps(eps)) != GRN_OK) return st;
   const size_t need = workspace_need(rows);
   if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
-  const void* acts[5] = {x, g, dy, dx, dg};
-  st = check_buffers(rows, acts, 5, 3, w, workspace, need, dw,
+  const Act acts[6] = {{x, x_stride},   {g, g_stride},   {dy, dy_stride},
+                       {y, y_stride},   {dx, dx_stride}, {dg, dg_stride}};
+  st = check_buffers(rows, acts, 6, 3, w, workspace, need, dw,
                      kSupportedD * (dw_fp32 ? 4 : 2));
   if (st != GRN_OK) return st;
+  grn::RowStrides rs;
+  rs.x = x_stride;
+  rs.g = g_stride;
+  rs.y = y_stride;
+  rs.dy = dy_stride;
+  rs.dx = dx_stride;
+  rs.dg = dg_stride;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int max_wg = env_max_wg();
+  for (int pass = 0; pass < 2; ++pass) {
+    if (grn::launch_fwd(x, g, w, y, rs, rows, eps, max_wg, s) != hipSuccess)
+      return GRN_ERR_HIP;
+  }
   return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, workspace,
-                                    rows, eps, env_max_wg(),
-                                    static_cast<hipStream_t>(stream)));
+                                    rs, rows, eps, max_wg, s));
 }
 
 grn_status gated_rmsnorm_ckpt_step(const void* x, const void* g,
@@ -145,24 +256,9 @@ grn_status gated_rmsnorm_ckpt_step(const void* x, const void* g,
                                    int64_t rows, int32_t D, float eps,
                                    int32_t dtype, int32_t dw_fp32,
                                    void* stream) {
-  grn_status st = check_common(rows, D, dtype);
-  if (st != GRN_OK) return st;
-  if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
-  if ((st = check_eps(eps)) != GRN_OK) return st;
-  const size_t need = workspace_need(rows);
-  if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
-  const void* acts[6] = {x, g, dy, y, dx, dg};
-  st = check_buffers(rows, acts, 6, 3, w, workspace, need, dw,
-                     kSupportedD * (dw_fp32 ? 4 : 2));
-  if (st != GRN_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int max_wg = env_max_wg();
-  for (int pass = 0; pass < 2; ++pass) {
-    if (grn::launch_fwd(x, g, w, y, rows, eps, max_wg, s) != hipSuccess)
-      return GRN_ERR_HIP;
-  }
-  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, workspace,
-                                    rows, eps, max_wg, s));
+  return gated_rmsnorm_ckpt_step_strided(x, D, g, D, w, dy, D, y, D, dx, D, dg, D,
+                                         dw, workspace, workspace_bytes, rows, D,
+                                         eps, dtype, dw_fp32, stream);
 }
 
 grn_status gated_rmsnorm_workspace_init(void* workspace, size_t workspace_bytes,
@@ -178,9 +274,9 @@ const char* gated_rmsnorm_status_string(int32_t status) {
   switch (status) {
     case GRN_OK: return "GRN_OK: success";
     case GRN_ERR_NULL: return "GRN_ERR_NULL: a required pointer is NULL";
-    case GRN_ERR_SHAPE: return "GRN_ERR_SHAPE: D must be 128 and 0 <= rows <= 2^31-1";
+    case GRN_ERR_SHAPE: return "GRN_ERR_SHAPE: D must be 128, 0 <= rows <= 2^31-1, and D <= stride <= 2^24";
     case GRN_ERR_DTYPE: return "GRN_ERR_DTYPE: dtype must be BF16 and dw_fp32 0 or 1";
-    case GRN_ERR_ALIGN: return "GRN_ERR_ALIGN: a pointer is misaligned";
+    case GRN_ERR_ALIGN: return "GRN_ERR_ALIGN: a pointer or row stride is not 16-byte aligned";
     case GRN_ERR_ALIAS: return "GRN_ERR_ALIAS: an output overlaps another buffer";
     case GRN_ERR_WORKSPACE: return "GRN_ERR_WORKSPACE: workspace missing or too small";
     case GRN_ERR_EPS: return "GRN_ERR_EPS: eps must be finite and >= 0";

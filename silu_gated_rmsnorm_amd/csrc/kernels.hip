@@ -85,16 +85,28 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
 
+// Row pitch of a tensor in 16-byte units (a packed row of 128 BF16 is 16).
+// Lane l of a wave touches row 4u + l/16 of its tile, bytes
+// [16(l%16), 16(l%16)+16) of that row: offset (4u + l/16) * pitch + l%16.
+__device__ __forceinline__ uint32_t lane_offset(int lane, int u, uint32_t pitch) {
+  return (uint32_t)(kRowsPerAccess * u + lane / kLanesPerRow) * pitch +
+         (uint32_t)(lane & (kLanesPerRow - 1));
+}
+
 // --------------------------------------------------------------------------
-// Forward.  A wave tile is U groups of 4 consecutive rows (4U rows, U KiB
-// per tensor, contiguous).  Lane l reads 16 bytes at u32x4 offset l + 64u
-// from the tile base: columns [8(l%16), 8(l%16)+8) of tile row 4u + l/16.
-// Waves walk the tiles with a grid stride.
+// Forward.  A wave tile is U groups of 4 consecutive rows (4U rows).  Lane l
+// owns columns [8(l%16), 8(l%16)+8) of tile row 4u + l/16.  With packed rows
+// (pitch 16) a tile is U contiguous KiB per tensor and lane l reads offset
+// l + 64u.  Waves walk the tiles with a grid stride.
+
+struct FwdPitch {
+  uint32_t x, g, y;  // row pitches in 16-byte units
+};
 
 template <int U, bool kFull>
 __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
                                          const u32x4* __restrict__ gb,
-                                         u32x4* __restrict__ yb,
+                                         u32x4* __restrict__ yb, FwdPitch pt,
                                          const float (&wf)[kVec], float eps,
                                          int lane, int nvalid) {
   const int sub = lane / kLanesPerRow;
@@ -102,8 +114,8 @@ __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (kFull || kRowsPerAccess * u + sub < nvalid) {
-      xv[u] = ld_stream<(GRN_FWD_NTL & 1) != 0>(xb + (uint32_t)(lane + kWave * u));
-      gv[u] = ld_stream<(GRN_FWD_NTL & 2) != 0>(gb + (uint32_t)(lane + kWave * u));
+      xv[u] = ld_stream<(GRN_FWD_NTL & 1) != 0>(xb + lane_offset(lane, u, pt.x));
+      gv[u] = ld_stream<(GRN_FWD_NTL & 2) != 0>(gb + lane_offset(lane, u, pt.g));
     } else {
       xv[u] = u32x4{0, 0, 0, 0};
       gv[u] = u32x4{0, 0, 0, 0};
@@ -126,7 +138,7 @@ __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
       yf[e] = (xf[e] * r) * wf[e] * s;
     }
     if (kFull || kRowsPerAccess * u + sub < nvalid)
-      st_stream<(GRN_FWD_NTS & 1) != 0>(yb + (uint32_t)(lane + kWave * u),
+      st_stream<(GRN_FWD_NTS & 1) != 0>(yb + lane_offset(lane, u, pt.y),
                                          pack_bf16x8(yf));
   }
 }
@@ -134,8 +146,8 @@ __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
 template <int U>
 __global__ void __launch_bounds__(kBlock)
 fwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
-           const u32x4* __restrict__ w, u32x4* __restrict__ y, int64_t rows,
-           float eps, int64_t ntiles) {
+           const u32x4* __restrict__ w, u32x4* __restrict__ y, FwdPitch pt,
+           int64_t rows, float eps, int64_t ntiles) {
   constexpr int kTileRows = kRowsPerAccess * U;
   const int lane = threadIdx.x & (kWave - 1);
   float wf[kVec];
@@ -145,18 +157,20 @@ fwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave_index();
        t < ntiles; t += nwaves) {
     const int64_t row0 = t * kTileRows;
-    const int64_t base = row0 * kLanesPerRow;  // in u32x4 units
+    const u32x4* xb = x + row0 * pt.x;
+    const u32x4* gb = g + row0 * pt.g;
+    u32x4* yb = y + row0 * pt.y;
     if (row0 + kTileRows <= rows) {
-      fwd_tile<U, true>(x + base, g + base, y + base, wf, eps, lane, kTileRows);
+      fwd_tile<U, true>(xb, gb, yb, pt, wf, eps, lane, kTileRows);
     } else {
-      fwd_tile<U, false>(x + base, g + base, y + base, wf, eps, lane,
-                         (int)(rows - row0));
+      fwd_tile<U, false>(xb, gb, yb, pt, wf, eps, lane, (int)(rows - row0));
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// Backward, dx/dg and one partial dw per chunk of kChunkRows rows.
+// Backward, dx/dg and one partial dw per chunk of R rows (R depends only on
+// the number of rows: chunk_rows_for()).
 //
 // The dw order is fixed by the chunk alone: within chunk c, wave v of the
 // workgroup takes step `it` on rows c*R + (it*4 + v)*4U + 4u + l/16, and
@@ -172,20 +186,23 @@ struct BwdRaw {
   u32x4 x[U], g[U], dy[U];
 };
 
+struct BwdPitch {
+  uint32_t x, g, dy, dx, dg;  // row pitches in 16-byte units
+};
+
 template <int U, bool kFull>
 __device__ __forceinline__ void bwd_load(BwdRaw<U>& r,
                                          const u32x4* __restrict__ xb,
                                          const u32x4* __restrict__ gb,
                                          const u32x4* __restrict__ dyb,
-                                         int lane, int nvalid) {
+                                         BwdPitch pt, int lane, int nvalid) {
   const int sub = lane / kLanesPerRow;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t o = (uint32_t)(lane + kWave * u);
     if (kFull || kRowsPerAccess * u + sub < nvalid) {
-      r.x[u] = ld_stream<(GRN_BWD_NTL & 1) != 0>(xb + o);
-      r.g[u] = ld_stream<(GRN_BWD_NTL & 2) != 0>(gb + o);
-      r.dy[u] = ld_stream<(GRN_BWD_NTL & 4) != 0>(dyb + o);
+      r.x[u] = ld_stream<(GRN_BWD_NTL & 1) != 0>(xb + lane_offset(lane, u, pt.x));
+      r.g[u] = ld_stream<(GRN_BWD_NTL & 2) != 0>(gb + lane_offset(lane, u, pt.g));
+      r.dy[u] = ld_stream<(GRN_BWD_NTL & 4) != 0>(dyb + lane_offset(lane, u, pt.dy));
     } else {
       r.x[u] = u32x4{0, 0, 0, 0};
       r.g[u] = u32x4{0, 0, 0, 0};
@@ -197,7 +214,7 @@ __device__ __forceinline__ void bwd_load(BwdRaw<U>& r,
 template <int U, bool kFull>
 __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
                                             u32x4* __restrict__ dxb,
-                                            u32x4* __restrict__ dgb,
+                                            u32x4* __restrict__ dgb, BwdPitch pt,
                                             const float (&wf)[kVec], float eps,
                                             int lane, int nvalid,
                                             float (&acc)[kVec]) {
@@ -237,9 +254,10 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
       q[e] *= n;  // dw contribution dy n s
     }
     if (kFull || kRowsPerAccess * u + sub < nvalid) {
-      const uint32_t o = (uint32_t)(lane + kWave * u);
-      st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + o, pack_bf16x8(dxf));
-      st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + o, pack_bf16x8(dgf));
+      st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset(lane, u, pt.dx),
+                                         pack_bf16x8(dxf));
+      st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset(lane, u, pt.dg),
+                                         pack_bf16x8(dgf));
 #pragma unroll
       for (int e = 0; e < kVec; ++e) acc[e] += q[e];
     }
@@ -250,18 +268,18 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
 // rows row0(it) = chunk0 + (it*4 + wave)*4U.  The loads of step it+1 are
 // issued before the arithmetic of step it, so every wave keeps a step of
 // reads in flight while it computes.
-template <int U, int kWaves, bool kFull>
+template <int U, int kWaves, int R, bool kFull>
 __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
                                           const u32x4* __restrict__ g,
                                           const u32x4* __restrict__ dy,
                                           u32x4* __restrict__ dx,
-                                          u32x4* __restrict__ dg,
+                                          u32x4* __restrict__ dg, BwdPitch pt,
                                           const float (&wf)[kVec], float eps,
                                           int64_t chunk0, int64_t rows,
                                           int wave, int lane,
                                           float (&acc)[kVec]) {
   constexpr int kStepRows = kRowsPerAccess * U;
-  constexpr int kIters = kChunkRows / (kWaves * kStepRows);
+  constexpr int kIters = R / (kWaves * kStepRows);
   auto row_of = [&](int it) {
     return chunk0 + (int64_t)(it * kWaves + wave) * kStepRows;
   };
@@ -273,24 +291,22 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
   // step it is computed.
   constexpr int kDepth = GRN_BWD_PREFETCH + 1;
   BwdRaw<U> buf[kDepth];
+  auto load = [&](BwdRaw<U>& b, int it) {
+    const int64_t row0 = row_of(it);
+    bwd_load<U, kFull>(b, x + row0 * pt.x, g + row0 * pt.g, dy + row0 * pt.dy, pt,
+                       lane, nvalid_of(it));
+  };
 #pragma unroll
   for (int k = 0; k < kDepth - 1; ++k) {
-    if (k < kIters) {
-      const int64_t base = row_of(k) * kLanesPerRow;
-      bwd_load<U, kFull>(buf[k], x + base, g + base, dy + base, lane, nvalid_of(k));
-    }
+    if (k < kIters) load(buf[k], k);
   }
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int ahead = it + kDepth - 1;
-    if (ahead < kIters) {
-      const int64_t base = row_of(ahead) * kLanesPerRow;
-      bwd_load<U, kFull>(buf[ahead % kDepth], x + base, g + base, dy + base, lane,
-                         nvalid_of(ahead));
-    }
-    const int64_t base = row_of(it) * kLanesPerRow;
-    bwd_compute<U, kFull>(buf[it % kDepth], dx + base, dg + base, wf, eps, lane,
-                          nvalid_of(it), acc);
+    if (ahead < kIters) load(buf[ahead % kDepth], ahead);
+    const int64_t row0 = row_of(it);
+    bwd_compute<U, kFull>(buf[it % kDepth], dx + row0 * pt.dx, dg + row0 * pt.dg, pt,
+                          wf, eps, lane, nvalid_of(it), acc);
   }
 }
 
@@ -382,7 +398,7 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 // The backward: dx and dg row by row, and dw through a fixed-order tree.
 //
 // dw tree (every level in a fixed order, so the bits depend only on rows):
-//  1. chunk c (kChunkRows rows, one workgroup): each lane adds its rows in
+//  1. chunk c (R rows, one workgroup): each lane adds its rows in
 //     step order, then the 16 lane/wave accumulators of a column are added
 //     in index order -> partial[c];
 //  2. group g (chunks [g*G, g*G + G), G = ceil(sqrt(nchunks))): the
@@ -399,18 +415,18 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 #define GRN_BWD_OCCUPANCY
 #endif
 
-template <int U, int kWaves>
+template <int U, int kWaves, int R>
 __global__ void __launch_bounds__(kWaves * kWave) GRN_BWD_OCCUPANCY
 bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, const u32x4* __restrict__ dy,
-           u32x4* __restrict__ dx, u32x4* __restrict__ dg,
+           u32x4* __restrict__ dx, u32x4* __restrict__ dg, BwdPitch pt,
            float* __restrict__ partial, float* __restrict__ gpart,
            uint32_t* __restrict__ counters, void* __restrict__ dw,
            int dw_fp32, int64_t rows, float eps, int64_t nchunks,
            int64_t group_size, int64_t ngroups) {
   constexpr int kThreads = kWaves * kWave;
   constexpr int kStepRows = kRowsPerAccess * U;                 // per wave
-  static_assert(kChunkRows % (kWaves * kStepRows) == 0,
+  static_assert(R % (kWaves * kStepRows) == 0,
                 "a chunk must be a whole number of workgroup steps");
   constexpr int kContrib = kWaves * kRowsPerAccess;
   __shared__ float red[kContrib][kD];
@@ -428,11 +444,13 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     float acc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
-    const int64_t chunk0 = c * kChunkRows;
-    if (chunk0 + kChunkRows <= rows) {
-      bwd_chunk<U, kWaves, true>(x, g, dy, dx, dg, wf, eps, chunk0, rows, wave, lane, acc);
+    const int64_t chunk0 = c * R;
+    if (chunk0 + R <= rows) {
+      bwd_chunk<U, kWaves, R, true>(x, g, dy, dx, dg, pt, wf, eps, chunk0, rows, wave,
+                                 lane, acc);
     } else {
-      bwd_chunk<U, kWaves, false>(x, g, dy, dx, dg, wf, eps, chunk0, rows, wave, lane, acc);
+      bwd_chunk<U, kWaves, R, false>(x, g, dy, dx, dg, pt, wf, eps, chunk0, rows, wave,
+                                  lane, acc);
     }
 
     // Level 1: the 16 accumulators of each column, in index order.
@@ -530,7 +548,7 @@ DeviceInfo device_info() {
             hipSuccess || info.fwd_blocks_per_cu <= 0)
       info.fwd_blocks_per_cu = 4;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &info.bwd_blocks_per_cu, bwd_kernel<kBwdU, kBwdWaves>,
+            &info.bwd_blocks_per_cu, bwd_kernel<kBwdU, kBwdWaves, kChunkRows>,
             kBwdWaves * kWave, 0) !=
             hipSuccess || info.bwd_blocks_per_cu <= 0)
       info.bwd_blocks_per_cu = 4;
@@ -564,7 +582,8 @@ BwdLayout bwd_layout(int64_t rows) {
     L.bytes = kCounterBytes;
     return L;
   }
-  L.nchunks = (rows + kChunkRows - 1) / kChunkRows;
+  L.chunk_rows = chunk_rows_for(rows);
+  L.nchunks = (rows + L.chunk_rows - 1) / L.chunk_rows;
   int64_t gs = 1;
   while (gs * gs < L.nchunks) ++gs;  // ceil(sqrt(nchunks)), at most 4096
   L.group_size = gs;
@@ -576,8 +595,11 @@ BwdLayout bwd_layout(int64_t rows) {
 }
 
 hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
-                      int64_t rows, float eps, int max_wg, hipStream_t s) {
+                      const RowStrides& st, int64_t rows, float eps, int max_wg,
+                      hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  const FwdPitch pt{(uint32_t)(st.x / kVec), (uint32_t)(st.g / kVec),
+                    (uint32_t)(st.y / kVec)};
   const DeviceInfo info = device_info();
   const int64_t ntiles = (rows + kRowsPerAccess * kFwdU - 1) /
                          (kRowsPerAccess * kFwdU);
@@ -588,16 +610,19 @@ hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
   hipLaunchKernelGGL(fwd_kernel<kFwdU>, dim3((unsigned)grid), dim3(kBlock), 0,
                      s, static_cast<const u32x4*>(x),
                      static_cast<const u32x4*>(g),
-                     static_cast<const u32x4*>(w), static_cast<u32x4*>(y),
+                     static_cast<const u32x4*>(w), static_cast<u32x4*>(y), pt,
                      rows, eps, ntiles);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
-                      int dw_fp32, void* workspace, int64_t rows, float eps,
-                      int max_wg, hipStream_t s) {
+                      int dw_fp32, void* workspace, const RowStrides& st,
+                      int64_t rows, float eps, int max_wg, hipStream_t s) {
   const BwdLayout L = bwd_layout(rows);
+  const BwdPitch pt{(uint32_t)(st.x / kVec), (uint32_t)(st.g / kVec),
+                    (uint32_t)(st.dy / kVec), (uint32_t)(st.dx / kVec),
+                    (uint32_t)(st.dg / kVec)};
   if (L.nchunks == 0) {
     hipLaunchKernelGGL(dw_zero_kernel, dim3(1), dim3(kD), 0, s, dw, dw_fp32);
     return hipGetLastError();
@@ -607,17 +632,17 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
   const int64_t resident =
       GRN_BWD_WG_PER_CU < 0 ? 0 : (int64_t)info.cus * info.bwd_blocks_per_cu;
   const int64_t grid = cap_grid(L.nchunks, resident, max_wg);
-  hipLaunchKernelGGL((bwd_kernel<kBwdU, kBwdWaves>), dim3((unsigned)grid),
-                     dim3(kBwdWaves * kWave), 0,
-                     s, static_cast<const u32x4*>(x),
-                     static_cast<const u32x4*>(g),
-                     static_cast<const u32x4*>(w),
-                     static_cast<const u32x4*>(dy), static_cast<u32x4*>(dx),
-                     static_cast<u32x4*>(dg),
-                     reinterpret_cast<float*>(ws + L.partial_off),
-                     reinterpret_cast<float*>(ws + L.gpart_off),
-                     reinterpret_cast<uint32_t*>(ws), dw, dw_fp32, rows, eps,
-                     L.nchunks, L.group_size, L.ngroups);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kBwdWaves * kWave), 0, s,
+                       static_cast<const u32x4*>(x), static_cast<const u32x4*>(g),
+                       static_cast<const u32x4*>(w), static_cast<const u32x4*>(dy),
+                       static_cast<u32x4*>(dx), static_cast<u32x4*>(dg), pt,
+                       reinterpret_cast<float*>(ws + L.partial_off),
+                       reinterpret_cast<float*>(ws + L.gpart_off),
+                       reinterpret_cast<uint32_t*>(ws), dw, dw_fp32, rows, eps,
+                       L.nchunks, L.group_size, L.ngroups);
+  };
+  launch(bwd_kernel<kBwdU, kBwdWaves, kChunkRows>);
   return hipGetLastError();
 }
 

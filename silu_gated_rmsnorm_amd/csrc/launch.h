@@ -9,12 +9,17 @@
 namespace grn {
 
 // Rows per dw chunk.  The backward adds the dw contributions of chunk
-// [c*kChunkRows, (c+1)*kChunkRows) into one FP32 partial; the chunking, and
-// therefore the bits of dw, depend only on the number of rows.
+// [c*R, (c+1)*R) into one FP32 partial, one workgroup per chunk; R, and
+// therefore the bits of dw, depend only on the number of rows.  One size
+// serves all row counts: smaller chunks for small problems (32 or 64 rows
+// below 196,608 rows) measured slower on MI355X, because the extra partials
+// and hand-offs cost more than the added parallelism gains.
 #ifndef GRN_CHUNK_ROWS
 #define GRN_CHUNK_ROWS 128
 #endif
 constexpr int kChunkRows = GRN_CHUNK_ROWS;
+
+constexpr int chunk_rows_for(int64_t /*rows*/) { return kChunkRows; }
 
 // Workspace of the backward, in this order:
 //   counters  uint32[kCounterWords]  arrival counters (zero between calls)
@@ -25,6 +30,7 @@ constexpr int kCounterWords = kMaxGroups + 1;
 constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
 
 struct BwdLayout {
+  int64_t chunk_rows = 0;
   int64_t nchunks = 0;
   int64_t group_size = 1;
   int64_t ngroups = 0;
@@ -35,13 +41,21 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(int64_t rows);
 
+// Row strides of the activations, in elements (each a multiple of 8, i.e.
+// 16-byte rows, and at most kMaxStride).  Packed rows have stride 128.
+struct RowStrides {
+  int64_t x = 128, g = 128, y = 128, dy = 128, dx = 128, dg = 128;
+};
+constexpr int64_t kMaxStride = int64_t{1} << 24;
+
 hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
-                      int64_t rows, float eps, int max_wg, hipStream_t s);
+                      const RowStrides& st, int64_t rows, float eps, int max_wg,
+                      hipStream_t s);
 
 hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
-                      int dw_fp32, void* workspace, int64_t rows, float eps,
-                      int max_wg, hipStream_t s);
+                      int dw_fp32, void* workspace, const RowStrides& st,
+                      int64_t rows, float eps, int max_wg, hipStream_t s);
 
 hipError_t launch_counters_zero(void* workspace, hipStream_t s);
 

@@ -28,7 +28,7 @@ def addr(k):
 
 
 X, G, W, DY, Y, DX, DG, DW, WS = (addr(k) for k in range(9))
-WS_BYTES = 32768 + 512 + 512    # counters + 1 chunk partial + 1 group partial
+WS_BYTES = 32768 + 512 + 512    # counters + 1 chunk partial + 1 group partial (10 rows)
 
 
 def declared_functions():
@@ -44,18 +44,21 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert sorted(binding._SIGS) == names
 
 
 def test_workspace_bytes(lib):
-    R = lib.gated_rmsnorm_chunk_rows()
     C = lib.gated_rmsnorm_workspace_init_bytes()
-    assert R == 128 and C == 32768
+    assert C == 32768
+    assert lib.gated_rmsnorm_chunk_rows(0) == 0
+    for rows in (1, 49488, 196608, 12582912):
+        assert lib.gated_rmsnorm_chunk_rows(rows) == 128
 
     def expect(rows):
+        R = lib.gated_rmsnorm_chunk_rows(rows)
         chunks = math.ceil(rows / R)
         gs = math.isqrt(chunks - 1) + 1 if chunks > 1 else 1   # ceil(sqrt(chunks))
         return C + (chunks + math.ceil(chunks / gs)) * 512
@@ -64,9 +67,10 @@ def test_workspace_bytes(lib):
     assert lib.gated_rmsnorm_workspace_bytes(-5, 128) == 0
     assert lib.gated_rmsnorm_workspace_bytes(10, 64) == 0
     assert lib.gated_rmsnorm_workspace_bytes(1, 128) == C + 1024
-    assert lib.gated_rmsnorm_workspace_bytes(R, 128) == C + 1024
-    assert lib.gated_rmsnorm_workspace_bytes(R + 1, 128) == C + 3 * 512
-    for rows in (5 * R, 17 * R + 3, 368832, 1572864, 12582912, 2**31 - 1):
+    assert lib.gated_rmsnorm_workspace_bytes(128, 128) == C + 1024
+    assert lib.gated_rmsnorm_workspace_bytes(129, 128) == C + 3 * 512
+    for rows in (5 * 128, 17 * 128 + 3, 49488, 196607, 196608, 368832, 1572864, 12582912,
+                 2**31 - 1):
         assert lib.gated_rmsnorm_workspace_bytes(rows, 128) == expect(rows), rows
     assert lib.gated_rmsnorm_workspace_bytes(2**31, 128) == 0
 
@@ -121,6 +125,41 @@ def test_bwd_rejects(lib, kw, code):
 ])
 def test_ckpt_rejects(lib, kw, code):
     assert ckpt(lib, **kw) == code
+
+
+def fwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, y=Y, sy=128, rows=ROWS, D=128, eps=1e-6):
+    return lib.gated_rmsnorm_fwd_strided(x, sx, g, sg, w, y, sy, rows, D, eps, 0, None)
+
+
+def bwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, dy=DY, sdy=128, dx=DX, sdx=128, dg=DG,
+          sdg=128, dw=DW, ws=WS, ws_bytes=WS_BYTES, rows=ROWS, eps=1e-6, dw_fp32=1):
+    return lib.gated_rmsnorm_bwd_strided(x, sx, g, sg, w, dy, sdy, dx, sdx, dg, sdg, dw, ws,
+                                         ws_bytes, rows, 128, eps, 0, dw_fp32, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sx=64), SHAPE), (dict(sg=127), SHAPE), (dict(sy=0), SHAPE), (dict(sx=-128), SHAPE),
+    (dict(sx=(1 << 24) + 8), SHAPE), (dict(sx=132), ALIGN), (dict(sy=136 + 4), ALIGN),
+    (dict(x=None), NULL),
+    # y rows interleaved with x's rows (same pitch) but sharing 16 bytes per row
+    (dict(sx=256, sy=256, y=X + 240), ALIAS),
+    # y overlapping g with a different pitch (conservative range test)
+    (dict(sg=256, sy=384, y=G + 256), ALIAS),
+])
+def test_fwd_strided_rejects(lib, kw, code):
+    assert fwd_s(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sdx=120), SHAPE), (dict(sdg=204), ALIGN),
+    # dx and dg as the halves of one buffer, but dg starting 16 bytes too early
+    (dict(sdx=256, sdg=256, dg=DX + 240), ALIAS),
+    # dg written over dy's rows
+    (dict(sdy=256, sdg=256, dg=DY), ALIAS),
+    (dict(sx=256, sdx=256, dx=X + 128), ALIAS),
+])
+def test_bwd_strided_rejects(lib, kw, code):
+    assert bwd_s(lib, **kw) == code
 
 
 def test_workspace_init_rejects(lib):

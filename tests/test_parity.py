@@ -20,8 +20,9 @@ pytestmark = pytest.mark.gpu
 EPS = 1e-6
 
 
-@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 15, 16, 17, 31, 63, 64, 65, 255, 256,
-                                  257, 511, 513, 1000, 4099, 12345])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255,
+                                  256, 257, 511, 513, 1000, 4099, 12345,
+                                  196607, 196608, 196609])
 def test_small_and_ragged(rows):
     say(f"[parity] ragged rows={rows}")
     inp = make_inputs(rows, seed=rows, device="cuda")
@@ -201,3 +202,73 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     u16 = assert_dw_close(dw16, dw_ref, False)
     say(f"  dw fp32 rel err {e32:.2e}, dw bf16 worst {u16} ulp")
+
+
+# --------------------------------------------------------------------------
+# Strided rows: x and g as the two halves of a fused projection, outputs
+# into strided views.  Results must be bitwise those of packed copies.
+
+def _bits_equal(a, b):
+    return torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
+
+
+@pytest.mark.parametrize("rows,pitch", [(5000, 256), (1037, 136), (300, 1024), (1, 256)])
+def test_strided_rows_match_packed(rows, pitch):
+    say(f"[parity] strided rows={rows} pitch={pitch}")
+    inp = make_inputs(rows, seed=31, device="cuda")
+    proj = torch.full((rows, pitch * 2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    x = proj[:, :128]
+    g = proj[:, pitch:pitch + 128]
+    x.copy_(inp["x"])
+    g.copy_(inp["g"])
+    dy_buf = torch.full((rows, pitch), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dy = dy_buf[:, pitch - 128:]
+    dy.copy_(inp["dy"])
+    y_buf = torch.full((rows, pitch), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = y_buf[:, 8:136] if pitch >= 136 else y_buf[:, :128]
+    dproj = torch.full((rows, pitch * 2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dx = dproj[:, :128]
+    dg = dproj[:, pitch:pitch + 128]
+    keep_y = y_buf.clone()
+    keep_d = dproj.clone()
+
+    binding.gated_rmsnorm_fwd(x, g, inp["w"], EPS, y=y)
+    _, _, dw = binding.gated_rmsnorm_bwd(x, g, inp["w"], dy, EPS, True, dx=dx, dg=dg)
+    y_p = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], EPS)
+    dx_p, dg_p, dw_p = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], EPS,
+                                                 True)
+    torch.cuda.synchronize()
+    assert _bits_equal(y, y_p) and _bits_equal(dx, dx_p) and _bits_equal(dg, dg_p)
+    assert torch.equal(dw.view(torch.int32), dw_p.view(torch.int32))
+    # nothing outside the strided rows was written
+    y_mask = torch.ones_like(y_buf, dtype=torch.bool)
+    y_mask[:, 8:136] = False if pitch >= 136 else y_mask[:, 8:136]
+    if pitch < 136:
+        y_mask[:, :128] = False
+    assert _bits_equal(y_buf[y_mask], keep_y[y_mask])
+    d_mask = torch.ones_like(dproj, dtype=torch.bool)
+    d_mask[:, :128] = False
+    d_mask[:, pitch:pitch + 128] = False
+    assert _bits_equal(dproj[d_mask], keep_d[d_mask])
+    y_ref, dx_ref, dg_ref, dw_ref = oracle_all(inp, EPS)
+    assert_acts_close("y", y, y_ref)
+    assert_acts_close("dx", dx, dx_ref)
+    assert_acts_close("dg", dg, dg_ref)
+    assert_dw_close(dw, dw_ref, True)
+
+
+def test_strided_ckpt_step_matches_packed():
+    rows, pitch = 4099, 256
+    say(f"[parity] strided ckpt rows={rows}")
+    inp = make_inputs(rows, seed=32, device="cuda")
+    proj = torch.empty((rows, 2 * pitch), dtype=torch.bfloat16, device="cuda")
+    x, g = proj[:, :128], proj[:, pitch:pitch + 128]
+    x.copy_(inp["x"])
+    g.copy_(inp["g"])
+    out = torch.empty((rows, 3 * pitch), dtype=torch.bfloat16, device="cuda")
+    y, dx, dg = out[:, :128], out[:, pitch:pitch + 128], out[:, 2 * pitch:2 * pitch + 128]
+    binding.gated_rmsnorm_ckpt_step(x, g, inp["w"], inp["dy"], EPS, False, y=y, dx=dx, dg=dg)
+    ref = binding.gated_rmsnorm_ckpt_step(inp["x"], inp["g"], inp["w"], inp["dy"], EPS, False)
+    torch.cuda.synchronize()
+    for a, b in zip((y, dx, dg), ref[:3]):
+        assert _bits_equal(a, b)
