@@ -53,6 +53,9 @@ R200_7684x48_US = {
 }
 
 COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
+# The deterministic backward kernel (template arguments: row groups per wave
+# step, waves per workgroup, rows per chunk, prefetched steps, deterministic).
+BWD_KERNEL = "grn::bwd_kernel<4, 4, 128, 1, true>"
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 
@@ -158,13 +161,13 @@ def main():
             check(lib.gated_rmsnorm_fwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["y"]), rows,
                                         D, eps, 0, S()))
 
-    def op_bwd(st, fp32=False):
+    def op_bwd(st, fp32=False, det=True):
         dw = st["dw32"] if fp32 else st["dw16"]
-        if fused:
+        if fused or not det:
             check(lib.gated_rmsnorm_bwd_strided(
                 P(st["x"]), R_(st["x"]), P(st["g"]), R_(st["g"]), P(st["w"]), P(st["dy"]),
                 R_(st["dy"]), P(st["dx"]), R_(st["dx"]), P(st["dg"]), R_(st["dg"]), P(dw),
-                P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), S()))
+                P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), int(det), S()))
         else:
             check(lib.gated_rmsnorm_bwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
                                         P(st["dx"]), P(st["dg"]), P(dw), P(st["ws"]),
@@ -176,7 +179,8 @@ def main():
             check(lib.gated_rmsnorm_ckpt_step_strided(
                 P(st["x"]), R_(st["x"]), P(st["g"]), R_(st["g"]), P(st["w"]), P(st["dy"]),
                 R_(st["dy"]), P(st["y"]), R_(st["y"]), P(st["dx"]), R_(st["dx"]), P(st["dg"]),
-                R_(st["dg"]), P(dw), P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), S()))
+                R_(st["dg"]), P(dw), P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), 1,
+                S()))
         else:
             check(lib.gated_rmsnorm_ckpt_step(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
                                               P(st["y"]), P(st["dx"]), P(st["dg"]), P(dw),
@@ -252,6 +256,10 @@ def main():
         bwd_us = rotate_time(op_bwd, R)
         rec("bwd", bwd_us, bwd_bytes)
         rec("bwd_f32", rotate_time(lambda st: op_bwd(st, True), R), bwd32_bytes)
+        # A/B: dw summed with float atomics instead of the fixed-order tree.
+        rec("bwd_nondet", rotate_time(lambda st: op_bwd(st, False, False), R), bwd_bytes)
+        rec("bwd_nondet_f32", rotate_time(lambda st: op_bwd(st, True, False), R),
+            bwd32_bytes)
         rec("ckpt", rotate_time(op_ckpt, R), ckpt_bytes)
         rec("ckpt_f32", rotate_time(lambda st: op_ckpt(st, True), R), ckpt32_bytes)
         rec("fwd+bwd", step_us, step_bytes)
@@ -262,6 +270,7 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         kinds = {"fwdg": (op_fwd, fwd_bytes), "bwdg": (op_bwd, bwd_bytes),
                  "bwdg_f32": (lambda st: op_bwd(st, True), bwd32_bytes),
+                 "bwdg_nondet_f32": (lambda st: op_bwd(st, True, False), bwd32_bytes),
                  "ckptg": (op_ckpt, ckpt_bytes),
                  "stepg_f32": (lambda st: op_ckpt(st, True), ckpt32_bytes)}
         for name, (fn, nbytes) in kinds.items():
@@ -286,6 +295,8 @@ def main():
         nb = max(2 * nsets, 20)
         for name, (fn, nbytes) in (("fwd_batched", (op_fwd, fwd_bytes)),
                                    ("bwd_batched", (op_bwd, bwd_bytes)),
+                                   ("bwd_nondet_batched",
+                                    (lambda st: op_bwd(st, False, False), bwd_bytes)),
                                    ("step_batched", (op_step, step_bytes)),
                                    ("ckpt_batched", (op_ckpt, ckpt_bytes))):
             gr = torch.cuda.CUDAGraph()
@@ -323,7 +334,7 @@ def main():
         # (rows > 0), timed over back-to-back launches on its stream.
         per_launch = bwd_bytes
         achieved = per_launch / (bwd_us * 1e-6) / 1e9
-        roofline = {"kernel": "grn::bwd_kernel<2>", "bound": "hbm",
+        roofline = {"kernel": BWD_KERNEL, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic_from_counters(),

@@ -81,7 +81,8 @@ typedef enum grn_status {
     GRN_ERR_ALIAS = 5,     /* an output overlaps an input, output or ws      */
     GRN_ERR_WORKSPACE = 6, /* workspace missing or smaller than required     */
     GRN_ERR_EPS = 7,       /* eps is negative, infinite or NaN               */
-    GRN_ERR_HIP = 8        /* the HIP runtime reported a launch error        */
+    GRN_ERR_HIP = 8,       /* the HIP runtime reported a launch error        */
+    GRN_ERR_ARG = 9        /* a flag argument (deterministic) is not 0 or 1  */
 } grn_status;
 
 enum { GRN_DTYPE_BF16 = 0 };
@@ -149,7 +150,15 @@ grn_status gated_rmsnorm_ckpt_step(const void *x, const void *g,
 /* Strided forms.  Same as the plain entry points, with each activation's
  * row stride in elements (see Layout above).  Invalid strides:
  * stride < D or > 2^24 -> GRN_ERR_SHAPE; not a multiple of 8 -> GRN_ERR_ALIGN.
- * Results are bitwise those of the plain entry points on packed copies. */
+ * Results are bitwise those of the plain entry points on packed copies.
+ *
+ * `deterministic` (backward and checkpointed step): 1 gives the fixed-order
+ * dw of the plain entry points.  0 adds each 128-row chunk's FP32 partial
+ * into one of 16 FP32 accumulators with float atomics (flashinfer PR #8701
+ * ships such a non-deterministic package beside the deterministic one, PR
+ * description): dw then agrees within FP32 rounding but its bits may differ
+ * from run to run.  dx and dg are the same bits either way, and the same
+ * workspace (and size) serves both.  Other values -> GRN_ERR_ARG. */
 grn_status gated_rmsnorm_fwd_strided(const void *x, int64_t x_stride,
                                      const void *g, int64_t g_stride,
                                      const void *w, void *y, int64_t y_stride,
@@ -165,14 +174,15 @@ grn_status gated_rmsnorm_bwd_strided(const void *x, int64_t x_stride,
                                      void *workspace, size_t workspace_bytes,
                                      int64_t rows, int32_t D, float eps,
                                      int32_t dtype, int32_t dw_fp32,
-                                     void *stream);
+                                     int32_t deterministic, void *stream);
 
 grn_status gated_rmsnorm_ckpt_step_strided(
     const void *x, int64_t x_stride, const void *g, int64_t g_stride,
     const void *w, const void *dy, int64_t dy_stride, void *y, int64_t y_stride,
     void *dx, int64_t dx_stride, void *dg, int64_t dg_stride, void *dw,
     void *workspace, size_t workspace_bytes, int64_t rows, int32_t D,
-    float eps, int32_t dtype, int32_t dw_fp32, void *stream);
+    float eps, int32_t dtype, int32_t dw_fp32, int32_t deterministic,
+    void *stream);
 
 /* Zero the arrival counters at the front of a workspace (the first
  * gated_rmsnorm_workspace_init_bytes() bytes) by enqueueing a small kernel

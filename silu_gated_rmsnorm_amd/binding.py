@@ -58,13 +58,14 @@ _SIGS = {
                                                     _VP, _I64, _VP, _I64, _VP, _VP,
                                                     ctypes.c_size_t, _I64, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32,
-                                                    ctypes.c_int32, _VP]),
+                                                    ctypes.c_int32, ctypes.c_int32, _VP]),
     "gated_rmsnorm_ckpt_step_strided": (ctypes.c_int32, [_VP, _I64, _VP, _I64, _VP, _VP,
                                                           _I64, _VP, _I64, _VP, _I64, _VP,
                                                           _I64, _VP, _VP, ctypes.c_size_t,
                                                           _I64, ctypes.c_int32,
                                                           ctypes.c_float, ctypes.c_int32,
-                                                          ctypes.c_int32, _VP]),
+                                                          ctypes.c_int32, ctypes.c_int32,
+                                                          _VP]),
     "gated_rmsnorm_workspace_init": (ctypes.c_int32, [_VP, ctypes.c_size_t, _VP]),
     "gated_rmsnorm_workspace_init_bytes": (ctypes.c_size_t, []),
     "gated_rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -179,8 +180,10 @@ def gated_rmsnorm_fwd(x, g, w, eps: float = 1e-6, y=None):
 
 
 def gated_rmsnorm_bwd(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
-                      dx=None, dg=None, dw=None, workspace=None):
-    """Gradients of sum(dy * y): returns (dx, dg, dw); dw is FP32 if dw_fp32."""
+                      dx=None, dg=None, dw=None, workspace=None, deterministic: bool = True):
+    """Gradients of sum(dy * y): returns (dx, dg, dw); dw is FP32 if dw_fp32.
+
+    deterministic=False sums dw with float atomics (bits may vary per run)."""
     lib = load_library()
     rows = x.shape[0]
     (px, sx), (pg, sg), pw = _act("x", x), _act("g", g, rows), _weight(w)
@@ -190,7 +193,7 @@ def gated_rmsnorm_bwd(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
     (pdx, sdx), (pdg, sdg) = _act("dx", dx, rows), _act("dg", dg, rows)
     dw = _dw(dw, dw_fp32, x.device)
     ws, ws_bytes = _workspace(rows, x.device, workspace)
-    if sx == sg == sdy == sdx == sdg == D_SUPPORTED:
+    if deterministic and sx == sg == sdy == sdx == sdg == D_SUPPORTED:
         st = lib.gated_rmsnorm_bwd(px, pg, pw, pdy, pdx, pdg, dw.data_ptr(), ws.data_ptr(),
                                    ws_bytes, rows, D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
                                    int(bool(dw_fp32)), _stream(x))
@@ -198,13 +201,15 @@ def gated_rmsnorm_bwd(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
         st = lib.gated_rmsnorm_bwd_strided(px, sx, pg, sg, pw, pdy, sdy, pdx, sdx, pdg, sdg,
                                            dw.data_ptr(), ws.data_ptr(), ws_bytes, rows,
                                            D_SUPPORTED, float(eps), GRN_DTYPE_BF16,
-                                           int(bool(dw_fp32)), _stream(x))
+                                           int(bool(dw_fp32)), int(bool(deterministic)),
+                                           _stream(x))
     _check(st)
     return dx, dg, dw
 
 
 def gated_rmsnorm_ckpt_step(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
-                            y=None, dx=None, dg=None, dw=None, workspace=None):
+                            y=None, dx=None, dg=None, dw=None, workspace=None,
+                            deterministic: bool = True):
     """Forward, recomputed forward, backward: returns (y, dx, dg, dw)."""
     lib = load_library()
     rows = x.shape[0]
@@ -217,7 +222,7 @@ def gated_rmsnorm_ckpt_step(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = Fals
                                         _act("dg", dg, rows))
     dw = _dw(dw, dw_fp32, x.device)
     ws, ws_bytes = _workspace(rows, x.device, workspace)
-    if sx == sg == sdy == sy == sdx == sdg == D_SUPPORTED:
+    if deterministic and sx == sg == sdy == sy == sdx == sdg == D_SUPPORTED:
         st = lib.gated_rmsnorm_ckpt_step(px, pg, pw, pdy, py, pdx, pdg, dw.data_ptr(),
                                          ws.data_ptr(), ws_bytes, rows, D_SUPPORTED,
                                          float(eps), GRN_DTYPE_BF16, int(bool(dw_fp32)),
@@ -227,7 +232,7 @@ def gated_rmsnorm_ckpt_step(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = Fals
                                                  sdx, pdg, sdg, dw.data_ptr(), ws.data_ptr(),
                                                  ws_bytes, rows, D_SUPPORTED, float(eps),
                                                  GRN_DTYPE_BF16, int(bool(dw_fp32)),
-                                                 _stream(x))
+                                                 int(bool(deterministic)), _stream(x))
     _check(st)
     return y, dx, dg, dw
 

@@ -182,10 +182,11 @@ grn_status gated_rmsnorm_bwd_strided(const void* x, int64_t x_stride,
                                      void* workspace, size_t workspace_bytes,
                                      int64_t rows, int32_t D, float eps,
                                      int32_t dtype, int32_t dw_fp32,
-                                     void* stream) {
+                                     int32_t deterministic, void* stream) {
   grn_status st = check_common(rows, D, dtype);
   if (st != GRN_OK) return st;
   if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
+  if (deterministic != 0 && deterministic != 1) return GRN_ERR_ARG;
   if ((st = check_eps(eps)) != GRN_OK) return st;
   const size_t need = workspace_need(rows);
   if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
@@ -200,8 +201,8 @@ grn_status gated_rmsnorm_bwd_strided(const void* x, int64_t x_stride,
   rs.dy = dy_stride;
   rs.dx = dx_stride;
   rs.dg = dg_stride;
-  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, workspace,
-                                    rs, rows, eps, env_max_wg(),
+  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, deterministic,
+                                    workspace, rs, rows, eps, env_max_wg(),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -212,7 +213,7 @@ grn_status gated_rmsnorm_bwd(const void* x, const void* g, const void* w,
                              int32_t dtype, int32_t dw_fp32, void* stream) {
   return gated_rmsnorm_bwd_strided(x, D, g, D, w, dy, D, dx, D, dg, D, dw,
                                    workspace, workspace_bytes, rows, D, eps,
-                                   dtype, dw_fp32, stream);
+                                   dtype, dw_fp32, 1, stream);
 }
 
 grn_status gated_rmsnorm_ckpt_step_strided(
@@ -220,10 +221,12 @@ grn_status gated_rmsnorm_ckpt_step_strided(
     const void* w, const void* dy, int64_t dy_stride, void* y, int64_t y_stride,
     void* dx, int64_t dx_stride, void* dg, int64_t dg_stride, void* dw,
     void* workspace, size_t workspace_bytes, int64_t rows, int32_t D,
-    float eps, int32_t dtype, int32_t dw_fp32, void* stream) {
+    float eps, int32_t dtype, int32_t dw_fp32, int32_t deterministic,
+    void* stream) {
   grn_status st = check_common(rows, D, dtype);
   if (st != GRN_OK) return st;
   if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
+  if (deterministic != 0 && deterministic != 1) return GRN_ERR_ARG;
   if ((st = check_eps(eps)) != GRN_OK) return st;
   const size_t need = workspace_need(rows);
   if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
@@ -245,8 +248,8 @@ grn_status gated_rmsnorm_ckpt_step_strided(
     if (grn::launch_fwd(x, g, w, y, rs, rows, eps, max_wg, s) != hipSuccess)
       return GRN_ERR_HIP;
   }
-  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, workspace,
-                                    rs, rows, eps, max_wg, s));
+  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, deterministic,
+                                    workspace, rs, rows, eps, max_wg, s));
 }
 
 grn_status gated_rmsnorm_ckpt_step(const void* x, const void* g,
@@ -258,7 +261,7 @@ grn_status gated_rmsnorm_ckpt_step(const void* x, const void* g,
                                    void* stream) {
   return gated_rmsnorm_ckpt_step_strided(x, D, g, D, w, dy, D, y, D, dx, D, dg, D,
                                          dw, workspace, workspace_bytes, rows, D,
-                                         eps, dtype, dw_fp32, stream);
+                                         eps, dtype, dw_fp32, 1, stream);
 }
 
 grn_status gated_rmsnorm_workspace_init(void* workspace, size_t workspace_bytes,
@@ -281,6 +284,7 @@ const char* gated_rmsnorm_status_string(int32_t status) {
     case GRN_ERR_WORKSPACE: return "GRN_ERR_WORKSPACE: workspace missing or too small";
     case GRN_ERR_EPS: return "GRN_ERR_EPS: eps must be finite and >= 0";
     case GRN_ERR_HIP: return "GRN_ERR_HIP: the HIP runtime reported a launch error";
+    case GRN_ERR_ARG: return "GRN_ERR_ARG: a flag argument is not 0 or 1";
     default: return "unknown gated_rmsnorm status";
   }
 }

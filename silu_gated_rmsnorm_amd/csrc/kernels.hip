@@ -29,7 +29,7 @@
 #define GRN_FWD_U 2          // row groups of 4 per wave tile in the forward
 #endif
 #ifndef GRN_BWD_U
-#define GRN_BWD_U 2          // row groups of 4 per wave step in the backward
+#define GRN_BWD_U 4          // row groups of 4 per wave step in the backward
 #endif
 #ifndef GRN_FWD_WG_PER_CU
 #define GRN_FWD_WG_PER_CU -1 // forward grid cap per CU; 0 = occupancy limit,
@@ -43,7 +43,10 @@
 #endif
 #ifndef GRN_BWD_PREFETCH
 #define GRN_BWD_PREFETCH 1   // steps of loads kept in flight ahead of the one
-#endif                       // being computed (0 = none)
+#endif                       // being computed (0 = none), deterministic dw
+#ifndef GRN_BWD_ND_PREFETCH
+#define GRN_BWD_ND_PREFETCH 0  // the same for the non-deterministic dw kernel
+#endif
 #ifndef GRN_SUM_BATCH
 #define GRN_SUM_BATCH 8      // partial rows per thread per round trip in the dw tree
 #endif
@@ -268,7 +271,7 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
 // rows row0(it) = chunk0 + (it*4 + wave)*4U.  The loads of step it+1 are
 // issued before the arithmetic of step it, so every wave keeps a step of
 // reads in flight while it computes.
-template <int U, int kWaves, int R, bool kFull>
+template <int U, int kWaves, int R, int kPrefetch, bool kFull>
 __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
                                           const u32x4* __restrict__ g,
                                           const u32x4* __restrict__ dy,
@@ -289,7 +292,7 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
   };
   // A ring of kDepth register buffers: step it+kDepth-1 is loaded while
   // step it is computed.
-  constexpr int kDepth = GRN_BWD_PREFETCH + 1;
+  constexpr int kDepth = kPrefetch + 1;
   BwdRaw<U> buf[kDepth];
   auto load = [&](BwdRaw<U>& b, int it) {
     const int64_t row0 = row_of(it);
@@ -409,13 +412,18 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 // Arrival counters live at the front of the workspace; each is returned to
 // zero by the workgroup that consumes it, so a zero-filled workspace stays
 // ready for the next call.
+#ifndef GRN_BWD_REDUCERS
+#define GRN_BWD_REDUCERS 1
+#endif
+constexpr bool kReducers = GRN_BWD_REDUCERS != 0;
+
 #if GRN_BWD_MIN_WAVES > 0
 #define GRN_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(GRN_BWD_MIN_WAVES)))
 #else
 #define GRN_BWD_OCCUPANCY
 #endif
 
-template <int U, int kWaves, int R>
+template <int U, int kWaves, int R, int kPrefetch, bool kDet>
 __global__ void __launch_bounds__(kWaves * kWave) GRN_BWD_OCCUPANCY
 bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, const u32x4* __restrict__ dy,
@@ -440,41 +448,101 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   float wf[kVec];
   unpack_bf16x8(w[col], wf);
 
-  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+  // Level 1 for chunk c: dx and dg of its rows, and the column sums of its
+  // dw terms (each lane's rows in step order, then the 16 lane/wave
+  // accumulators of a column in index order); valid in threads 0..127.
+  auto chunk_partial = [&](int64_t c) {
     float acc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
     const int64_t chunk0 = c * R;
     if (chunk0 + R <= rows) {
-      bwd_chunk<U, kWaves, R, true>(x, g, dy, dx, dg, pt, wf, eps, chunk0, rows, wave,
-                                 lane, acc);
+      bwd_chunk<U, kWaves, R, kPrefetch, true>(x, g, dy, dx, dg, pt, wf, eps, chunk0, rows,
+                                               wave, lane, acc);
     } else {
-      bwd_chunk<U, kWaves, R, false>(x, g, dy, dx, dg, pt, wf, eps, chunk0, rows, wave,
-                                  lane, acc);
+      bwd_chunk<U, kWaves, R, kPrefetch, false>(x, g, dy, dx, dg, pt, wf, eps, chunk0, rows,
+                                                wave, lane, acc);
     }
-
-    // Level 1: the 16 accumulators of each column, in index order.
     const int contrib = wave * kRowsPerAccess + sub;
 #pragma unroll
     for (int e = 0; e < kVec; ++e) red[contrib][col * kVec + e] = acc[e];
     __syncthreads();
+    float v = 0.0f;
     if (t < kD) {
-      float v = 0.0f;
 #pragma unroll
       for (int k = 0; k < kContrib; ++k) v += red[k][t];
-      store_coherent(partial + c * kD + t, v);
-      wait_memory();  // the partial is complete before anyone arrives
     }
-    __syncthreads();
+    return v;
+  };
 
-    // Level 2: the last chunk of group grp to finish sums the group.
-    const int64_t grp = c / group_size;
+  // Work items: chunks [0, nchunks), then (deterministic dw) one reducer
+  // item per group, which arrives at its group's counter like a chunk but
+  // carries no partial.  Being last in the grid, reducers usually arrive
+  // after all of their group's chunks, so most group sums run once the
+  // streaming is done instead of amid it.
+  const int64_t nwork = nchunks + (kDet && kReducers ? ngroups : 0);
+  for (int64_t item = blockIdx.x; item < nwork; item += gridDim.x) {
+    int64_t grp = item - nchunks;  // for a reducer item
+    if (item < nchunks) {
+      const int64_t c = item;
+      const float v = chunk_partial(c);
+      if constexpr (!kDet) {
+        // Non-deterministic dw: the chunk sum is added with float atomics
+        // into one of kNondetSlots FP32 accumulators (chunk c uses slot
+        // c mod slots, so concurrent chunks hit different addresses); the
+        // last chunk to arrive adds the slots and returns them to zero.  The
+        // order of the atomic adds, and so the bits of dw, vary per run.
+        float* accum = reinterpret_cast<float*>(counters) + kNondetAccum;
+        if (t < kD) {
+          __hip_atomic_fetch_add(accum + (c % kNondetSlots) * kD + t, v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+          wait_memory();
+        }
+        __syncthreads();
+        if (t == 0)
+          last_overall = __hip_atomic_fetch_add(&counters[kMaxGroups], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) ==
+                         (uint32_t)(nchunks - 1);
+        __syncthreads();
+        if (last_overall) {
+          if (t < kD) {
+            float slot[kNondetSlots];
+#pragma unroll
+            for (int k = 0; k < kNondetSlots; ++k)
+              slot[k] = __hip_atomic_load(accum + k * kD + t, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+            float total = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kNondetSlots; ++k) total += slot[k];
+            store_dw(dw, dw_fp32, t, total);
+#pragma unroll
+            for (int k = 0; k < kNondetSlots; ++k)
+              __hip_atomic_store(accum + k * kD + t, 0.0f, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (t == 0)
+            __hip_atomic_store(&counters[kMaxGroups], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        continue;
+      }
+      if (t < kD) {
+        store_coherent(partial + c * kD + t, v);
+        wait_memory();  // the partial is complete before anyone arrives
+      }
+      __syncthreads();
+      grp = c / group_size;
+    }
+
+    // Level 2: the last arrival at group grp's counter (its chunks, plus its
+    // reducer item) sums the group.
     const int64_t gbeg = grp * group_size;
     const int64_t gcnt = (nchunks - gbeg) < group_size ? (nchunks - gbeg) : group_size;
+    const uint32_t arrivals = (uint32_t)gcnt + (kReducers ? 1u : 0u);
     if (t == 0)
       last_in_group = __hip_atomic_fetch_add(&counters[grp], 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) ==
-                      (uint32_t)(gcnt - 1);
+                                             __HIP_MEMORY_SCOPE_AGENT) == arrivals - 1u;
     __syncthreads();
     if (last_in_group) {
       float* lds = &red[0][0];
@@ -517,10 +585,15 @@ counters_zero_kernel(uint32_t* __restrict__ counters) {
 // --------------------------------------------------------------------------
 // Launchers.
 
+
 namespace {
 
 constexpr int kFwdU = GRN_FWD_U;
-constexpr int kBwdU = GRN_BWD_U;
+// The two backward kernels.  Each has its own prefetch depth: the one that
+// measured fastest for it (the register budgets of the two differ).
+constexpr auto kBwdDet = bwd_kernel<GRN_BWD_U, GRN_BWD_WAVES, kChunkRows, GRN_BWD_PREFETCH, true>;
+constexpr auto kBwdNondet =
+    bwd_kernel<GRN_BWD_U, GRN_BWD_WAVES, kChunkRows, GRN_BWD_ND_PREFETCH, false>;
 constexpr int kBwdWaves = GRN_BWD_WAVES;
 
 struct DeviceInfo {
@@ -548,7 +621,7 @@ DeviceInfo device_info() {
             hipSuccess || info.fwd_blocks_per_cu <= 0)
       info.fwd_blocks_per_cu = 4;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &info.bwd_blocks_per_cu, bwd_kernel<kBwdU, kBwdWaves, kChunkRows>,
+            &info.bwd_blocks_per_cu, kBwdDet,
             kBwdWaves * kWave, 0) !=
             hipSuccess || info.bwd_blocks_per_cu <= 0)
       info.bwd_blocks_per_cu = 4;
@@ -617,8 +690,9 @@ hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
 
 hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
-                      int dw_fp32, void* workspace, const RowStrides& st,
-                      int64_t rows, float eps, int max_wg, hipStream_t s) {
+                      int dw_fp32, int deterministic, void* workspace,
+                      const RowStrides& st, int64_t rows, float eps, int max_wg,
+                      hipStream_t s) {
   const BwdLayout L = bwd_layout(rows);
   const BwdPitch pt{(uint32_t)(st.x / kVec), (uint32_t)(st.g / kVec),
                     (uint32_t)(st.dy / kVec), (uint32_t)(st.dx / kVec),
@@ -631,7 +705,8 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
   const DeviceInfo info = device_info();
   const int64_t resident =
       GRN_BWD_WG_PER_CU < 0 ? 0 : (int64_t)info.cus * info.bwd_blocks_per_cu;
-  const int64_t grid = cap_grid(L.nchunks, resident, max_wg);
+  const int64_t nwork = L.nchunks + (deterministic && kReducers ? L.ngroups : 0);
+  const int64_t grid = cap_grid(nwork, resident, max_wg);
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kBwdWaves * kWave), 0, s,
                        static_cast<const u32x4*>(x), static_cast<const u32x4*>(g),
@@ -642,7 +717,11 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                        reinterpret_cast<uint32_t*>(ws), dw, dw_fp32, rows, eps,
                        L.nchunks, L.group_size, L.ngroups);
   };
-  launch(bwd_kernel<kBwdU, kBwdWaves, kChunkRows>);
+  if (deterministic) {
+    launch(kBwdDet);
+  } else {
+    launch(kBwdNondet);
+  }
   return hipGetLastError();
 }
 

@@ -25,8 +25,22 @@ constexpr int chunk_rows_for(int64_t /*rows*/) { return kChunkRows; }
 //   counters  uint32[kCounterWords]  arrival counters (zero between calls)
 //   partial   float[nchunks][128]     one dw partial per chunk
 //   gpart     float[ngroups][128]     one dw partial per group of chunks
+// The counter region holds, as 32-bit words:
+//   [0, ngroups)                 one arrival counter per group (ngroups is at
+//                                most 4096: ceil(sqrt(nchunks)) <= 4096 for
+//                                nchunks <= 2^24, i.e. rows < 2^31)
+//   [kNondetAccum, +slots*128)   the FP32 accumulators of the
+//                                non-deterministic dw, kNondetSlots of them
+//   [kMaxGroups]                 the overall counter
 constexpr int kMaxGroups = 8191;
 constexpr int kCounterWords = kMaxGroups + 1;
+#ifndef GRN_NONDET_SLOTS
+#define GRN_NONDET_SLOTS 16
+#endif
+constexpr int kNondetSlots = GRN_NONDET_SLOTS;
+constexpr int kNondetAccum = 4096;
+static_assert(kNondetSlots >= 1 && kNondetAccum + kNondetSlots * 128 <= kMaxGroups,
+              "the non-deterministic accumulators must fit the counter region");
 constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
 
 struct BwdLayout {
@@ -54,8 +68,9 @@ hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
 
 hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
-                      int dw_fp32, void* workspace, const RowStrides& st,
-                      int64_t rows, float eps, int max_wg, hipStream_t s);
+                      int dw_fp32, int deterministic, void* workspace,
+                      const RowStrides& st, int64_t rows, float eps, int max_wg,
+                      hipStream_t s);
 
 hipError_t launch_counters_zero(void* workspace, hipStream_t s);
 

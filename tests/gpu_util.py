@@ -60,3 +60,16 @@ def assert_dw_close(dw_t, ref, dw_fp32):
     worst, ok = dw16_check(bits(dw_t), ref)
     assert ok, f"dw bf16 off by {worst} ulp (allowed {DW16_ULPS})"
     return worst
+
+
+def oracle_dw_streamed(inp, eps, chunk=1 << 20):
+    """Oracle dw over every row, in row chunks whose FP64 sums are added in order."""
+    rows = inp["x"].shape[0]
+    w = bits(inp["w"])
+    dw = np.zeros(128)
+    for r0 in range(0, rows, chunk):
+        sl = slice(r0, min(rows, r0 + chunk))
+        _, _, part = oracle.bwd(bits(inp["x"][sl]), bits(inp["g"][sl]), w,
+                                bits(inp["dy"][sl]), eps)
+        dw += part
+    return dw

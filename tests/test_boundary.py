@@ -17,7 +17,7 @@ from silu_gated_rmsnorm_amd import binding
 ROOT = pathlib.Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "gated_rmsnorm.h"
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, EPS, HIP = range(9)
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, EPS, HIP, ARG = range(10)
 ROWS = 10
 ACT = ROWS * 128 * 2            # bytes of one [10, 128] BF16 tensor
 BASE = 0x7F0000000000           # fake device addresses, 4 KiB apart
@@ -76,7 +76,7 @@ def test_workspace_bytes(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.gated_rmsnorm_status_string(code).decode()
         assert s.startswith("GRN_"), s
     assert "unknown" in lib.gated_rmsnorm_status_string(99).decode()
@@ -132,9 +132,15 @@ def fwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, y=Y, sy=128, rows=ROWS, D=128, eps
 
 
 def bwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, dy=DY, sdy=128, dx=DX, sdx=128, dg=DG,
-          sdg=128, dw=DW, ws=WS, ws_bytes=WS_BYTES, rows=ROWS, eps=1e-6, dw_fp32=1):
+          sdg=128, dw=DW, ws=WS, ws_bytes=WS_BYTES, rows=ROWS, eps=1e-6, dw_fp32=1, det=1):
     return lib.gated_rmsnorm_bwd_strided(x, sx, g, sg, w, dy, sdy, dx, sdx, dg, sdg, dw, ws,
-                                         ws_bytes, rows, 128, eps, 0, dw_fp32, None)
+                                         ws_bytes, rows, 128, eps, 0, dw_fp32, det, None)
+
+
+def ckpt_s(lib, det=1, dw_fp32=1, y=Y):
+    return lib.gated_rmsnorm_ckpt_step_strided(X, 128, G, 128, W, DY, 128, y, 128, DX, 128,
+                                               DG, 128, DW, WS, WS_BYTES, ROWS, 128, 1e-6, 0,
+                                               dw_fp32, det, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -157,9 +163,18 @@ def test_fwd_strided_rejects(lib, kw, code):
     # dg written over dy's rows
     (dict(sdy=256, sdg=256, dg=DY), ALIAS),
     (dict(sx=256, sdx=256, dx=X + 128), ALIAS),
+    (dict(det=2), ARG), (dict(det=-1), ARG), (dict(det=0, dw_fp32=3), DTYPE),
+    (dict(det=0, dx=None), NULL), (dict(det=0, ws_bytes=100), WORKSPACE),
 ])
 def test_bwd_strided_rejects(lib, kw, code):
     assert bwd_s(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(det=2), ARG), (dict(det=0, y=None), NULL), (dict(det=0, dw_fp32=7), DTYPE),
+])
+def test_ckpt_strided_rejects(lib, kw, code):
+    assert ckpt_s(lib, **kw) == code
 
 
 def test_workspace_init_rejects(lib):

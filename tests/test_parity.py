@@ -13,8 +13,8 @@ import oracle
 from silu_gated_rmsnorm_amd import binding
 from silu_gated_rmsnorm_amd.inputs import WORKLOADS, make_inputs, make_workload_inputs
 
-from gpu_util import (assert_acts_close, assert_dw_close, bits, f64, gpu_all,
-                      oracle_all, say)
+from gpu_util import (assert_acts_close, assert_dw_close, bits, f64, gpu_all, oracle_all,
+                      oracle_dw_streamed, say)
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
@@ -164,19 +164,6 @@ def _sample_rows(rows, extra=None, seed=0):
     return np.unique(idx)
 
 
-def _oracle_dw_streamed(inp, eps, chunk=1 << 20):
-    """Oracle dw over every row, in row chunks whose FP64 sums are added in order."""
-    rows = inp["x"].shape[0]
-    w = bits(inp["w"])
-    dw = np.zeros(128)
-    for r0 in range(0, rows, chunk):
-        sl = slice(r0, min(rows, r0 + chunk))
-        _, _, part = oracle.bwd(bits(inp["x"][sl]), bits(inp["g"][sl]), w,
-                                bits(inp["dy"][sl]), eps)
-        dw += part
-    return dw
-
-
 @pytest.mark.parametrize("name", ["7684x48", "32768x48", "65536x48", "262144x48_outliers"])
 def test_full_size_sampled(name):
     wl = WORKLOADS[name]
@@ -195,7 +182,7 @@ def test_full_size_sampled(name):
     assert_acts_close("y", y[idx], y_ref)
     assert_acts_close("dx", dx[idx], dx_ref)
     assert_acts_close("dg", dg[idx], dg_ref)
-    dw_ref = _oracle_dw_streamed(inp, wl.eps)
+    dw_ref = oracle_dw_streamed(inp, wl.eps)
     e32 = assert_dw_close(dw32, dw_ref, True)
     _, _, dw16 = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], wl.eps,
                                            dw_fp32=False)
