@@ -2,6 +2,7 @@
 """Benchmark of the SiLU-gated RMSNorm training forward + backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7684x48]
+                    [--dtype bf16|f16|f32] [--dim 64|128|256]
 
 A step is one training forward and backward over the workload: the forward
 (y from x, g, w) followed by the backward (dx, dg and the deterministic BF16
@@ -53,9 +54,10 @@ R200_7684x48_US = {
 }
 
 COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
-# The deterministic backward kernel (template arguments: row groups per wave
-# step, waves per workgroup, rows per chunk, prefetched steps, deterministic).
-BWD_KERNEL = "grn::bwd_kernel<4, 4, 128, 1, true>"
+# The deterministic backward kernel (template arguments: element type, D, row
+# groups per wave step, waves per workgroup, rows per chunk, prefetched
+# steps, deterministic).
+BWD_KERNEL = "grn::bwd_kernel<Dt::{dtype}, {D}, 4, 4, 128, 1, true>"
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 
@@ -69,9 +71,13 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="7684x48")
+    p.add_argument("--dtype", choices=("bf16", "f16", "f32"), default="bf16",
+                   help="storage type of x, g, dy, w and the outputs (the pages: bf16)")
+    p.add_argument("--dim", type=int, choices=(64, 128, 256), default=D,
+                   help="row width D (the pages: 128)")
     p.add_argument("--layout", choices=("packed", "fused"), default="packed",
                    help="packed rows, or x|g and dx|dg as the two halves of fused "
-                        "[rows, 256] buffers (row stride 256)")
+                        "[rows, 2D] buffers (row stride 2D)")
     p.add_argument("--op-reps", type=int, default=50,
                    help="launches per operation in the per-op timings")
     p.add_argument("--no-ops", action="store_true", help="skip per-op timings")
@@ -107,22 +113,30 @@ def main():
     import torch
 
     from silu_gated_rmsnorm_amd import binding
-    from silu_gated_rmsnorm_amd.inputs import WORKLOADS, make_workload_inputs
+    from silu_gated_rmsnorm_amd.inputs import WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     wl = WORKLOADS[args.workload]
     rows, eps = wl.rows, wl.eps
+    D = args.dim
+    tdtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[args.dtype]
+    dt_code = {"bf16": 0, "f16": 1, "f32": 2}[args.dtype]
+    esize = 4 if args.dtype == "f32" else 2
+    row_bytes = D * esize
+    default_shape = (args.dtype, D) == ("bf16", 128)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = binding.load_library()
-    tensor_bytes = rows * ROW_BYTES
+    tensor_bytes = rows * row_bytes
     nsets = math.ceil(ROTATION_BYTES / tensor_bytes) + 1
-    log(f"[bench] workload {wl.name}: rows={rows} D={D} eps={eps} "
+    log(f"[bench] workload {wl.name}: rows={rows} D={D} dtype={args.dtype} eps={eps} "
         f"buffer sets={nsets} lib={binding.library_path()}")
 
-    inp = make_workload_inputs(wl, device=dev)
-    ws_bytes = binding.gated_rmsnorm_workspace_bytes(rows)
+    inp = make_inputs(rows, D, seed=0, device=dev, g_std=wl.g_std,
+                      outlier_frac=wl.outlier_frac, outlier_scale=wl.outlier_scale,
+                      dtype=tdtype)
+    ws_bytes = binding.gated_rmsnorm_workspace_bytes(rows, D)
     fused = args.layout == "fused"
     sets = []
     for _ in range(nsets):
@@ -136,9 +150,9 @@ def main():
             for k in ("y", "dx", "dg"):
                 st[k] = torch.empty_like(inp["x"])
         st["w"] = inp["w"]
-        st["dw16"] = torch.empty(D, dtype=torch.bfloat16, device=dev)
+        st["dw16"] = torch.empty(D, dtype=tdtype, device=dev)   # dw in the input type
         st["dw32"] = torch.empty(D, dtype=torch.float32, device=dev)
-        st["ws"] = binding.new_workspace(rows, dev)
+        st["ws"] = binding.new_workspace(rows, dev, D)
         sets.append(st)
     torch.cuda.synchronize()
 
@@ -156,10 +170,10 @@ def main():
         if fused:
             check(lib.gated_rmsnorm_fwd_strided(P(st["x"]), R_(st["x"]), P(st["g"]),
                                                 R_(st["g"]), P(st["w"]), P(st["y"]),
-                                                R_(st["y"]), rows, D, eps, 0, S()))
+                                                R_(st["y"]), rows, D, eps, dt_code, S()))
         else:
             check(lib.gated_rmsnorm_fwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["y"]), rows,
-                                        D, eps, 0, S()))
+                                        D, eps, dt_code, S()))
 
     def op_bwd(st, fp32=False, det=True):
         dw = st["dw32"] if fp32 else st["dw16"]
@@ -167,11 +181,11 @@ def main():
             check(lib.gated_rmsnorm_bwd_strided(
                 P(st["x"]), R_(st["x"]), P(st["g"]), R_(st["g"]), P(st["w"]), P(st["dy"]),
                 R_(st["dy"]), P(st["dx"]), R_(st["dx"]), P(st["dg"]), R_(st["dg"]), P(dw),
-                P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), int(det), S()))
+                P(st["ws"]), ws_bytes, rows, D, eps, dt_code, int(fp32), int(det), S()))
         else:
             check(lib.gated_rmsnorm_bwd(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
                                         P(st["dx"]), P(st["dg"]), P(dw), P(st["ws"]),
-                                        ws_bytes, rows, D, eps, 0, int(fp32), S()))
+                                        ws_bytes, rows, D, eps, dt_code, int(fp32), S()))
 
     def op_ckpt(st, fp32=False):
         dw = st["dw32"] if fp32 else st["dw16"]
@@ -179,12 +193,12 @@ def main():
             check(lib.gated_rmsnorm_ckpt_step_strided(
                 P(st["x"]), R_(st["x"]), P(st["g"]), R_(st["g"]), P(st["w"]), P(st["dy"]),
                 R_(st["dy"]), P(st["y"]), R_(st["y"]), P(st["dx"]), R_(st["dx"]), P(st["dg"]),
-                R_(st["dg"]), P(dw), P(st["ws"]), ws_bytes, rows, D, eps, 0, int(fp32), 1,
-                S()))
+                R_(st["dg"]), P(dw), P(st["ws"]), ws_bytes, rows, D, eps, dt_code,
+                int(fp32), 1, S()))
         else:
             check(lib.gated_rmsnorm_ckpt_step(P(st["x"]), P(st["g"]), P(st["w"]), P(st["dy"]),
                                               P(st["y"]), P(st["dx"]), P(st["dg"]), P(dw),
-                                              P(st["ws"]), ws_bytes, rows, D, eps, 0,
+                                              P(st["ws"]), ws_bytes, rows, D, eps, dt_code,
                                               int(fp32), S()))
 
     def op_step(st):
@@ -194,9 +208,9 @@ def main():
     # Algorithmic bytes: what the method must move (inputs read once,
     # outputs written once, w and dw included; workspace traffic, ~0.4 % of
     # the backward's, is implementation overhead and not counted).
-    fwd_bytes = rows * 3 * ROW_BYTES + ROW_BYTES
-    bwd_bytes = rows * 5 * ROW_BYTES + ROW_BYTES + D * 2
-    bwd32_bytes = rows * 5 * ROW_BYTES + ROW_BYTES + D * 4
+    fwd_bytes = rows * 3 * row_bytes + row_bytes
+    bwd_bytes = rows * 5 * row_bytes + row_bytes + D * esize
+    bwd32_bytes = rows * 5 * row_bytes + row_bytes + D * 4
     ckpt_bytes = 2 * fwd_bytes + bwd_bytes
     ckpt32_bytes = 2 * fwd_bytes + bwd32_bytes
     step_bytes = fwd_bytes + bwd_bytes
@@ -221,7 +235,7 @@ def main():
         us = rotate_time(fn, args.op_reps)
         gbps = nbytes / (us * 1e-6) / 1e9
         print(json.dumps({"profile_op": args.profile_op, "workload": wl.name,
-                          "layout": args.layout,
+                          "layout": args.layout, "dtype": args.dtype, "D": D,
                           "launches": args.op_reps, "avg_us_events": round(us, 3),
                           "GB/s": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}),
               flush=True)
@@ -234,7 +248,7 @@ def main():
     step_us = rotate_time(op_step, args.steps)
     ms_per_step = step_us / 1e3
     value = step_bytes / (step_us * 1e-6) / 1e9
-    log(f"[bench] step (fwd + bwd, bf16 dw): {step_us:.2f} us, {value:.1f} GB/s "
+    log(f"[bench] step (fwd + bwd, {args.dtype} dw): {step_us:.2f} us, {value:.1f} GB/s "
         f"({100 * value / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
 
     ops = {}
@@ -334,19 +348,19 @@ def main():
         # (rows > 0), timed over back-to-back launches on its stream.
         per_launch = bwd_bytes
         achieved = per_launch / (bwd_us * 1e-6) / 1e9
-        roofline = {"kernel": BWD_KERNEL, "bound": "hbm",
+        roofline = {"kernel": BWD_KERNEL.format(dtype=args.dtype, D=D), "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic_from_counters(),
+                    "traffic": traffic_from_counters() if default_shape else None,
                     "bytes_per_launch": per_launch, "avg_us": round(bwd_us, 3)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.dtype == "bf16":
         cpu = cpu_baseline(inp, wl, fwd_bytes + bwd_bytes, args.cpu_seconds)
 
     out = {
         "metric": "achieved HBM GB/s (% of peak) + us, gated RMSNorm fwd/bwd at "
-                  f"{wl.name}x128 bf16",
+                  f"{wl.name}x{D} {args.dtype}",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -357,17 +371,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "io_dtype": "bf16",
-        "data": "synthetic (seeded normal BF16 inputs resident in HBM)",
+        "io_dtype": args.dtype,
+        "data": f"synthetic (seeded normal {args.dtype} inputs resident in HBM)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "rows": rows, "D": D,
                    "layout": args.layout,
-                   "eps": eps, "step": "fwd + bwd (deterministic BF16 dw)",
+                   "eps": eps, "step": f"fwd + bwd (deterministic {args.dtype} dw)",
                    "bytes_per_step": step_bytes, "buffer_sets": nsets},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": ops,
-        "context_r200_us": R200_7684x48_US if wl.name == "7684x48" else None,
+        "context_r200_us": R200_7684x48_US if wl.name == "7684x48" and default_shape else None,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)

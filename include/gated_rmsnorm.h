@@ -27,13 +27,16 @@
  *  - Layout: every activation (x, g, dy, y, dx, dg) is a row-major
  *    [rows, D] array.  The plain entry points take packed rows (row stride
  *    = D elements); the _strided ones take a row stride per activation, in
- *    elements: D <= stride <= 2^24 and a multiple of 8 (16-byte rows), e.g.
+ *    elements: D <= stride <= 2^24 and 16-byte rows (a multiple of 8
+ *    elements for BF16/FP16, of 4 for FP32), e.g.
  *    x and g as the two halves of a fused [rows, 2D] projection, which the
  *    commit 10c6017 message of flashinfer PR #8701 distinguishes from rows
  *    held packed.  w is [D].
- *  - dtype: GRN_DTYPE_BF16 is the only accepted element type.  Arithmetic is
- *    FP32; each BF16 output is rounded once, to nearest even.
- *  - D: only D = 128 is accepted (one row = 256 bytes).
+ *  - dtype: the element type of every activation and of w: GRN_DTYPE_BF16
+ *    (the type the pages measure), GRN_DTYPE_F16 or GRN_DTYPE_F32.
+ *    Arithmetic is FP32; each BF16/FP16 output is rounded once, to nearest
+ *    even (FP16 results beyond its range become infinite).
+ *  - D: 64, 128 or 256 (the pages measure D = 128).
  *  - rows: 0 <= rows <= GRN_MAX_ROWS.  rows = 0 is allowed: the forward does
  *    nothing, the backward writes dw = 0 (an empty sum).  Activation pointers
  *    may then be NULL.
@@ -43,13 +46,14 @@
  *    enqueued on `stream` (a hipStream_t; NULL is the default stream), so
  *    the calls may be captured into a HIP graph.
  *  - Alignment: activations, w and the workspace must be 16-byte aligned;
- *    dw 4-byte aligned (FP32) or 2-byte aligned (BF16).
+ *    dw aligned to its element size.
  *  - Aliasing: no output may overlap any input, another output or the
  *    workspace.  Rows of equal stride that interleave without sharing a
  *    byte (dx and dg as the two halves of one fused buffer) do not overlap;
- *    for unequal strides the check is on address ranges (conservative).  An in-place dx = x would let one workgroup overwrite rows
- *    that another has not read yet; the review of flashinfer PR #8878
- *    ("Follow-up" findings) reports that race for a sibling kernel.
+ *    for unequal strides the check is on address ranges (conservative).
+ *    An in-place dx = x would let one workgroup overwrite rows that another
+ *    has not read yet; the review of flashinfer PR #8878 ("Follow-up"
+ *    findings) reports that race for a sibling kernel.
  *  - eps: finite and >= 0.
  *  - Errors: arguments are checked before anything is enqueued; an invalid
  *    call returns a non-zero grn_status and enqueues nothing.  A failed
@@ -73,9 +77,10 @@ extern "C" {
 typedef enum grn_status {
     GRN_OK = 0,
     GRN_ERR_NULL = 1,      /* a required pointer is NULL                     */
-    GRN_ERR_SHAPE = 2,     /* D != 128, rows outside [0, GRN_MAX_ROWS], or
-                              a row stride outside [D, 2^24]                 */
-    GRN_ERR_DTYPE = 3,     /* dtype is not BF16, or dw_fp32 is not 0 or 1    */
+    GRN_ERR_SHAPE = 2,     /* D not 64/128/256, rows outside
+                              [0, GRN_MAX_ROWS], or a row stride outside
+                              [D, 2^24]                                      */
+    GRN_ERR_DTYPE = 3,     /* unknown dtype, or dw_fp32 is not 0 or 1        */
     GRN_ERR_ALIGN = 4,     /* a pointer, or a row stride, is not aligned as
                               required                                       */
     GRN_ERR_ALIAS = 5,     /* an output overlaps an input, output or ws      */
@@ -85,14 +90,15 @@ typedef enum grn_status {
     GRN_ERR_ARG = 9        /* a flag argument (deterministic) is not 0 or 1  */
 } grn_status;
 
-enum { GRN_DTYPE_BF16 = 0 };
+enum { GRN_DTYPE_BF16 = 0, GRN_DTYPE_F16 = 1, GRN_DTYPE_F32 = 2 };
 
 #define GRN_MAX_ROWS ((int64_t)2147483647)
 
-/* Bytes of device workspace the backward needs for `rows` rows of width D:
- * a fixed region of arrival counters, one FP32 partial dw of D values per
- * chunk of gated_rmsnorm_chunk_rows(rows) rows, and one per group of about
- * sqrt(chunks) chunks.  Returns 0 for rows <= 0 or an unsupported D.
+/* Bytes of device workspace the backward needs for `rows` rows of width D,
+ * for any element type: a fixed region of arrival counters, one FP32
+ * partial dw of D values per chunk of rows (at most 128 rows a chunk, see
+ * gated_rmsnorm_chunk_rows), and one per group of about sqrt(chunks)
+ * chunks.  Returns 0 for rows <= 0 or an unsupported D.
  *
  * Workspace contract: the counter region must be zero before the first
  * backward that uses the workspace (see gated_rmsnorm_workspace_init);
@@ -102,13 +108,15 @@ enum { GRN_DTYPE_BF16 = 0 };
  * not share a workspace. */
 size_t gated_rmsnorm_workspace_bytes(int64_t rows, int32_t D);
 
-/* Rows R in one dw chunk of a backward over `rows` rows: rows [c*R, (c+1)*R)
- * form chunk c.  R depends only on `rows` (it is 128 for every rows > 0 in
- * this version); 0 for rows <= 0. */
-int32_t gated_rmsnorm_chunk_rows(int64_t rows);
+/* Rows R in one dw chunk of a backward over `rows` rows of D values of type
+ * dtype: rows [c*R, (c+1)*R) form chunk c.  R depends only on the row size
+ * in bytes (in this version 256 for 128-byte rows, i.e. D = 64 in BF16 or
+ * FP16, and 128 otherwise, whatever `rows`); 0 for rows <= 0 or an
+ * unsupported D or dtype. */
+int32_t gated_rmsnorm_chunk_rows(int64_t rows, int32_t D, int32_t dtype);
 
 /* Forward: y = x * rsqrt(mean(x^2) + eps) * w * silu(g), row by row.
- * In:  x, g [rows, D] BF16; w [D] BF16.   Out: y [rows, D] BF16.
+ * In:  x, g [rows, D]; w [D].   Out: y [rows, D]; all of type dtype.
  * y of a row depends only on that row, w and eps: it is bitwise the same
  * whatever the launch shape. */
 grn_status gated_rmsnorm_fwd(const void *x, const void *g, const void *w,
@@ -120,10 +128,11 @@ grn_status gated_rmsnorm_fwd(const void *x, const void *g, const void *w,
  *   dx = r (dn - n c),  n = x r,  dn = dy w silu(g),  c = mean_j(dn n)
  *   dg = dy w n silu'(g)
  *   dw = sum over rows of dy n silu(g)          (overwritten, not added to)
- * In:  x, g, dy [rows, D] BF16; w [D] BF16; workspace of at least
+ * In:  x, g, dy [rows, D] and w [D] of type dtype; workspace of at least
  *      gated_rmsnorm_workspace_bytes(rows, D) bytes whose counter region is
  *      zero (see the workspace contract above; may be NULL when rows = 0).
- * Out: dx, dg [rows, D] BF16; dw [D], FP32 if dw_fp32 = 1, else BF16.
+ * Out: dx, dg [rows, D] of type dtype; dw [D], FP32 if dw_fp32 = 1, else
+ *      of type dtype.
  * dw is summed in FP32 in a fixed order that depends only on rows (per
  * chunk of rows, then per group of chunks, then over groups): it is
  * bit-identical from run to run and across launch shapes.  The whole
@@ -149,16 +158,18 @@ grn_status gated_rmsnorm_ckpt_step(const void *x, const void *g,
 
 /* Strided forms.  Same as the plain entry points, with each activation's
  * row stride in elements (see Layout above).  Invalid strides:
- * stride < D or > 2^24 -> GRN_ERR_SHAPE; not a multiple of 8 -> GRN_ERR_ALIGN.
+ * stride < D or > 2^24 -> GRN_ERR_SHAPE; rows not 16-byte aligned ->
+ * GRN_ERR_ALIGN.
  * Results are bitwise those of the plain entry points on packed copies.
  *
  * `deterministic` (backward and checkpointed step): 1 gives the fixed-order
- * dw of the plain entry points.  0 adds each 128-row chunk's FP32 partial
- * into one of 16 FP32 accumulators with float atomics (flashinfer PR #8701
- * ships such a non-deterministic package beside the deterministic one, PR
- * description): dw then agrees within FP32 rounding but its bits may differ
+ * dw of the plain entry points.  0 adds each chunk's FP32 partial with FP64
+ * atomics into one of a few accumulators (15 for D = 128), and the last
+ * chunk rounds their sum once (flashinfer PR #8701 ships such a
+ * non-deterministic package beside the deterministic one, PR description):
+ * dw then meets the same accuracy but its bits are not guaranteed to repeat
  * from run to run.  dx and dg are the same bits either way, and the same
- * workspace (and size) serves both.  Other values -> GRN_ERR_ARG. */
+ * workspace serves both.  Other values -> GRN_ERR_ARG. */
 grn_status gated_rmsnorm_fwd_strided(const void *x, int64_t x_stride,
                                      const void *g, int64_t g_stride,
                                      const void *w, void *y, int64_t y_stride,

@@ -8,8 +8,14 @@
 
 namespace {
 
-constexpr int32_t kSupportedD = 128;
-constexpr size_t kRowBytes = kSupportedD * 2;  // one BF16 row
+bool supported_d(int32_t D) { return D == 64 || D == 128 || D == 256; }
+
+bool supported_dtype(int32_t dtype) {
+  return dtype == GRN_DTYPE_BF16 || dtype == GRN_DTYPE_F16 || dtype == GRN_DTYPE_F32;
+}
+
+// Bytes per element of a supported dtype.
+int64_t elem_bytes(int32_t dtype) { return dtype == GRN_DTYPE_F32 ? 4 : 2; }
 
 // A set of `rows` rows of `width` bytes, `pitch` bytes apart, from `p`.
 struct Rows {
@@ -61,8 +67,8 @@ int env_max_wg() {
 }
 
 grn_status check_common(int64_t rows, int32_t D, int32_t dtype) {
-  if (D != kSupportedD || rows < 0 || rows > GRN_MAX_ROWS) return GRN_ERR_SHAPE;
-  if (dtype != GRN_DTYPE_BF16) return GRN_ERR_DTYPE;
+  if (!supported_d(D) || rows < 0 || rows > GRN_MAX_ROWS) return GRN_ERR_SHAPE;
+  if (!supported_dtype(dtype)) return GRN_ERR_DTYPE;
   return GRN_OK;
 }
 
@@ -73,14 +79,16 @@ grn_status check_eps(float eps) {
 
 // A row stride (elements) is at least D, at most kMaxStride, and keeps every
 // row 16-byte aligned.
-grn_status check_stride(int64_t stride) {
-  if (stride < kSupportedD || stride > grn::kMaxStride) return GRN_ERR_SHAPE;
-  if (stride % 8 != 0) return GRN_ERR_ALIGN;
+grn_status check_stride(int64_t stride, int32_t D, int64_t esize) {
+  if (stride < D || stride > grn::kMaxStride) return GRN_ERR_SHAPE;
+  if ((stride * esize) % 16 != 0) return GRN_ERR_ALIGN;
   return GRN_OK;
 }
 
-size_t workspace_need(int64_t rows) {
-  return rows > 0 ? grn::bwd_layout(rows).bytes : 0;
+// Workspace bytes of a call (esize > 0), or the most any element type needs
+// (esize = 0).
+size_t workspace_need(int64_t rows, int32_t D, int32_t esize) {
+  return rows > 0 ? grn::bwd_layout(rows, D, esize).bytes : 0;
 }
 
 struct Act {
@@ -88,11 +96,12 @@ struct Act {
   int64_t stride;  // elements
 };
 
-// Pointer rules shared by every entry point.  `acts` are [rows, D] BF16
-// activations (inputs first, then outputs); `n_in` of them are inputs.
-grn_status check_buffers(int64_t rows, const Act* acts, int n_acts, int n_in,
-                         const void* w, const void* ws, size_t ws_need,
-                         const void* dw, size_t dw_bytes) {
+// Pointer rules shared by every entry point.  `acts` are [rows, D]
+// activations of `esize`-byte elements (inputs first, then outputs); `n_in`
+// of them are inputs.  w is [D] of the same type; dw is `dw_bytes` bytes.
+grn_status check_buffers(int64_t rows, int32_t D, int64_t esize, const Act* acts,
+                         int n_acts, int n_in, const void* w, const void* ws,
+                         size_t ws_need, const void* dw, size_t dw_bytes) {
   if (w == nullptr) return GRN_ERR_NULL;
   if (rows > 0)
     for (int k = 0; k < n_acts; ++k)
@@ -101,27 +110,28 @@ grn_status check_buffers(int64_t rows, const Act* acts, int n_acts, int n_in,
   if (ws_need > 0 && ws == nullptr) return GRN_ERR_WORKSPACE;
 
   for (int k = 0; k < n_acts; ++k) {
-    const grn_status st = check_stride(acts[k].stride);
+    const grn_status st = check_stride(acts[k].stride, D, esize);
     if (st != GRN_OK) return st;
   }
   if (!aligned(w, 16)) return GRN_ERR_ALIGN;
   for (int k = 0; k < n_acts; ++k)
     if (!aligned(acts[k].p, 16)) return GRN_ERR_ALIGN;
   if (ws_need > 0 && !aligned(ws, 16)) return GRN_ERR_ALIGN;
-  if (dw_bytes > 0 && !aligned(dw, dw_bytes / kSupportedD)) return GRN_ERR_ALIGN;
+  if (dw_bytes > 0 && !aligned(dw, dw_bytes / D)) return GRN_ERR_ALIGN;
 
   // Outputs: activations n_in.., dw, and the workspace (written as scratch).
+  const int64_t row_bytes = D * esize;
   Rows outs[8];
   int n_out = 0;
   for (int k = n_in; k < n_acts; ++k)
-    outs[n_out++] = Rows{acts[k].p, rows, acts[k].stride * 2, (int64_t)kRowBytes};
+    outs[n_out++] = Rows{acts[k].p, rows, acts[k].stride * esize, row_bytes};
   if (dw_bytes > 0) outs[n_out++] = plain(dw, dw_bytes);
   if (ws_need > 0) outs[n_out++] = plain(ws, ws_need);
   Rows ins[8];
   int n_ins = 0;
   for (int k = 0; k < n_in; ++k)
-    ins[n_ins++] = Rows{acts[k].p, rows, acts[k].stride * 2, (int64_t)kRowBytes};
-  ins[n_ins++] = plain(w, kRowBytes);
+    ins[n_ins++] = Rows{acts[k].p, rows, acts[k].stride * esize, row_bytes};
+  ins[n_ins++] = plain(w, (size_t)row_bytes);
   for (int a = 0; a < n_out; ++a) {
     for (int b = 0; b < n_ins; ++b)
       if (overlap(outs[a], ins[b])) return GRN_ERR_ALIAS;
@@ -131,6 +141,11 @@ grn_status check_buffers(int64_t rows, const Act* acts, int n_acts, int n_in,
   return GRN_OK;
 }
 
+// Bytes of dw: FP32 if asked for, else the input type.
+size_t dw_size(int32_t D, int32_t dtype, int32_t dw_fp32) {
+  return (size_t)D * (dw_fp32 ? 4 : elem_bytes(dtype));
+}
+
 grn_status hip_status(hipError_t e) { return e == hipSuccess ? GRN_OK : GRN_ERR_HIP; }
 
 }  // namespace
@@ -138,12 +153,13 @@ grn_status hip_status(hipError_t e) { return e == hipSuccess ? GRN_OK : GRN_ERR_
 extern "C" {
 
 size_t gated_rmsnorm_workspace_bytes(int64_t rows, int32_t D) {
-  if (D != kSupportedD || rows <= 0 || rows > GRN_MAX_ROWS) return 0;
-  return workspace_need(rows);
+  if (!supported_d(D) || rows <= 0 || rows > GRN_MAX_ROWS) return 0;
+  return workspace_need(rows, D, 0);
 }
 
-int32_t gated_rmsnorm_chunk_rows(int64_t rows) {
-  return rows <= 0 ? 0 : grn::chunk_rows_for(rows);
+int32_t gated_rmsnorm_chunk_rows(int64_t rows, int32_t D, int32_t dtype) {
+  if (rows <= 0 || !supported_d(D) || !supported_dtype(dtype)) return 0;
+  return grn::chunk_rows_for(D * (int32_t)elem_bytes(dtype));
 }
 
 size_t gated_rmsnorm_workspace_init_bytes(void) { return grn::kCounterBytes; }
@@ -157,13 +173,13 @@ grn_status gated_rmsnorm_fwd_strided(const void* x, int64_t x_stride,
   if (st != GRN_OK) return st;
   if ((st = check_eps(eps)) != GRN_OK) return st;
   const Act acts[3] = {{x, x_stride}, {g, g_stride}, {y, y_stride}};
-  st = check_buffers(rows, acts, 3, 2, w, nullptr, 0, nullptr, 0);
+  st = check_buffers(rows, D, elem_bytes(dtype), acts, 3, 2, w, nullptr, 0, nullptr, 0);
   if (st != GRN_OK) return st;
   grn::RowStrides rs;
   rs.x = x_stride;
   rs.g = g_stride;
   rs.y = y_stride;
-  return hip_status(grn::launch_fwd(x, g, w, y, rs, rows, eps, env_max_wg(),
+  return hip_status(grn::launch_fwd(x, g, w, y, rs, rows, D, dtype, eps, env_max_wg(),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -188,12 +204,12 @@ grn_status gated_rmsnorm_bwd_strided(const void* x, int64_t x_stride,
   if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
   if (deterministic != 0 && deterministic != 1) return GRN_ERR_ARG;
   if ((st = check_eps(eps)) != GRN_OK) return st;
-  const size_t need = workspace_need(rows);
+  const size_t need = workspace_need(rows, D, (int32_t)elem_bytes(dtype));
   if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
   const Act acts[5] = {{x, x_stride}, {g, g_stride}, {dy, dy_stride},
                        {dx, dx_stride}, {dg, dg_stride}};
-  st = check_buffers(rows, acts, 5, 3, w, workspace, need, dw,
-                     kSupportedD * (dw_fp32 ? 4 : 2));
+  st = check_buffers(rows, D, elem_bytes(dtype), acts, 5, 3, w, workspace, need, dw,
+                     dw_size(D, dtype, dw_fp32));
   if (st != GRN_OK) return st;
   grn::RowStrides rs;
   rs.x = x_stride;
@@ -202,7 +218,7 @@ grn_status gated_rmsnorm_bwd_strided(const void* x, int64_t x_stride,
   rs.dx = dx_stride;
   rs.dg = dg_stride;
   return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, deterministic,
-                                    workspace, rs, rows, eps, env_max_wg(),
+                                    workspace, rs, rows, D, dtype, eps, env_max_wg(),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -228,12 +244,12 @@ grn_status gated_rmsnorm_ckpt_step_strided(
   if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
   if (deterministic != 0 && deterministic != 1) return GRN_ERR_ARG;
   if ((st = check_eps(eps)) != GRN_OK) return st;
-  const size_t need = workspace_need(rows);
+  const size_t need = workspace_need(rows, D, (int32_t)elem_bytes(dtype));
   if (workspace_bytes < need) return GRN_ERR_WORKSPACE;
   const Act acts[6] = {{x, x_stride},   {g, g_stride},   {dy, dy_stride},
                        {y, y_stride},   {dx, dx_stride}, {dg, dg_stride}};
-  st = check_buffers(rows, acts, 6, 3, w, workspace, need, dw,
-                     kSupportedD * (dw_fp32 ? 4 : 2));
+  st = check_buffers(rows, D, elem_bytes(dtype), acts, 6, 3, w, workspace, need, dw,
+                     dw_size(D, dtype, dw_fp32));
   if (st != GRN_OK) return st;
   grn::RowStrides rs;
   rs.x = x_stride;
@@ -245,11 +261,11 @@ grn_status gated_rmsnorm_ckpt_step_strided(
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int max_wg = env_max_wg();
   for (int pass = 0; pass < 2; ++pass) {
-    if (grn::launch_fwd(x, g, w, y, rs, rows, eps, max_wg, s) != hipSuccess)
+    if (grn::launch_fwd(x, g, w, y, rs, rows, D, dtype, eps, max_wg, s) != hipSuccess)
       return GRN_ERR_HIP;
   }
   return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, deterministic,
-                                    workspace, rs, rows, eps, max_wg, s));
+                                    workspace, rs, rows, D, dtype, eps, max_wg, s));
 }
 
 grn_status gated_rmsnorm_ckpt_step(const void* x, const void* g,
@@ -277,8 +293,8 @@ const char* gated_rmsnorm_status_string(int32_t status) {
   switch (status) {
     case GRN_OK: return "GRN_OK: success";
     case GRN_ERR_NULL: return "GRN_ERR_NULL: a required pointer is NULL";
-    case GRN_ERR_SHAPE: return "GRN_ERR_SHAPE: D must be 128, 0 <= rows <= 2^31-1, and D <= stride <= 2^24";
-    case GRN_ERR_DTYPE: return "GRN_ERR_DTYPE: dtype must be BF16 and dw_fp32 0 or 1";
+    case GRN_ERR_SHAPE: return "GRN_ERR_SHAPE: D must be 64, 128 or 256, 0 <= rows <= 2^31-1, and D <= stride <= 2^24";
+    case GRN_ERR_DTYPE: return "GRN_ERR_DTYPE: dtype must be BF16, FP16 or FP32 and dw_fp32 0 or 1";
     case GRN_ERR_ALIGN: return "GRN_ERR_ALIGN: a pointer or row stride is not 16-byte aligned";
     case GRN_ERR_ALIAS: return "GRN_ERR_ALIAS: an output overlaps another buffer";
     case GRN_ERR_WORKSPACE: return "GRN_ERR_WORKSPACE: workspace missing or too small";

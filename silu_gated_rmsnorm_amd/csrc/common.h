@@ -1,10 +1,12 @@
 // Device helpers shared by the gfx950 kernels of the SiLU-gated RMSNorm.
 //
-// Data layout the kernels rely on: one row of D = 128 BF16 values is 256
-// bytes, i.e. 16 lanes x one 16-byte access of 8 values.  A wave of 64
-// lanes therefore touches 4 consecutive rows (1 KiB, fully coalesced) per
-// load instruction, and the 16 lanes of one row are exactly one DPP "row"
-// of the wave, so a row sum is four DPP steps with no LDS and no barrier.
+// Data layout the kernels rely on: a row of D values is cut into 16-byte
+// lane accesses (8 BF16 or FP16 values, or 4 FP32 values), so a row spans
+// kLanes = D / values-per-access consecutive lanes and one wave access
+// covers 64 / kLanes consecutive rows (1 KiB, fully coalesced).  For the
+// main case, D = 128 BF16, that is 16 lanes per row and 4 rows per access,
+// and the 16 lanes of a row are exactly one DPP row of the wave.  Row sums
+// stay in registers: DPP within 16 lanes, a lane swap beyond.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,40 +14,112 @@
 
 namespace grn {
 
-constexpr int kD = 128;                              // row width (values)
-constexpr int kVec = 8;                              // BF16 values per lane access
-constexpr int kLanesPerRow = kD / kVec;              // 16
 constexpr int kWave = 64;                            // CDNA wavefront
-constexpr int kRowsPerAccess = kWave / kLanesPerRow; // 4 rows per wave access
 constexpr int kBlock = 256;                          // threads per workgroup
 constexpr int kWavesPerBlock = kBlock / kWave;       // 4
+constexpr int kMaxD = 256;                           // widest supported row
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 8 BF16 values (packed in 4 dwords, element 2k in the low half of dword k)
-// to FP32.  BF16 is the top half of binary32, so this is exact.
-__device__ __forceinline__ void unpack_bf16x8(u32x4 p, float (&f)[kVec]) {
+// Element types of the activations and the weight (the numeric values are
+// those of GRN_DTYPE_* in the C header).
+enum class Dt : int { bf16 = 0, f16 = 1, f32 = 2 };
+
+// Conversions between one 16-byte access and FP32 registers.  Values are
+// packed little-endian: element 2k in the low half of dword k for 16-bit
+// types.  Narrowing rounds to nearest, ties to even.
+template <Dt T>
+struct Codec;
+
+template <>
+struct Codec<Dt::bf16> {
+  static constexpr int kPer = 8;  // values per 16 bytes
+  // BF16 is the top half of binary32: widening is exact.
+  static __device__ __forceinline__ void unpack(u32x4 p, float (&f)[kPer]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    f[2 * k] = __uint_as_float(p[k] << 16);
-    f[2 * k + 1] = __uint_as_float(p[k] & 0xffff0000u);
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(p[k] << 16);
+      f[2 * k + 1] = __uint_as_float(p[k] & 0xffff0000u);
+    }
   }
-}
-
-// Two FP32 values to a BF16 pair, round to nearest even (gfx950 has a
-// native packed conversion, v_cvt_pk_bf16_f32, which this lowers to).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ u32x4 pack_bf16x8(const float (&f)[kVec]) {
-  u32x4 p;
+  // gfx950 has a native packed conversion, v_cvt_pk_bf16_f32, which this
+  // lowers to.
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&f)[kPer]) {
+    u32x4 p;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(f[2 * k], f[2 * k + 1]);
-  return p;
-}
+    for (int k = 0; k < 4; ++k) p[k] = pack2(f[2 * k], f[2 * k + 1]);
+    return p;
+  }
+  static __device__ __forceinline__ void store1(void* dst, int i, float v) {
+    static_cast<uint16_t*>(dst)[i] = (uint16_t)(pack2(v, 0.0f) & 0xffffu);
+  }
+};
+
+template <>
+struct Codec<Dt::f16> {
+  static constexpr int kPer = 8;
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ void unpack(u32x4 p, float (&f)[kPer]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // The element goes through a scalar first: a bit_cast applied to the
+      // vector element expression itself was compiled as a read of element
+      // 0 for every k.
+      const uint32_t d = p[k];
+      const f16x2 h = __builtin_bit_cast(f16x2, d);
+      f[2 * k] = (float)h.x;
+      f[2 * k + 1] = (float)h.y;
+    }
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&f)[kPer]) {
+    u32x4 p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = pack2(f[2 * k], f[2 * k + 1]);
+    return p;
+  }
+  static __device__ __forceinline__ void store1(void* dst, int i, float v) {
+    static_cast<_Float16*>(dst)[i] = (_Float16)v;
+  }
+};
+
+template <>
+struct Codec<Dt::f32> {
+  static constexpr int kPer = 4;
+  static __device__ __forceinline__ void unpack(u32x4 p, float (&f)[kPer]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(p[k]);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&f)[kPer]) {
+    u32x4 p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = __float_as_uint(f[k]);
+    return p;
+  }
+  static __device__ __forceinline__ void store1(void* dst, int i, float v) {
+    static_cast<float*>(dst)[i] = v;
+  }
+};
+
+// How a row of D values of type T sits on the lanes of a wave.
+template <Dt T, int D>
+struct Shape {
+  using C = Codec<T>;
+  static constexpr int kVec = C::kPer;              // values per lane access
+  static constexpr int kLanes = D / kVec;           // lanes per row
+  static constexpr int kRows = kWave / kLanes;      // rows per wave access
+  static_assert(D % kVec == 0, "a row is a whole number of 16-byte accesses");
+  static_assert(kLanes == 8 || kLanes == 16 || kLanes == 32 || kLanes == 64,
+                "a row spans 8, 16, 32 or 64 lanes");
+};
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -53,16 +127,20 @@ __device__ __forceinline__ float dpp_mov(float v) {
       __builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lanes of a DPP row, the result in all 16 lanes.  Steps:
-// swap neighbours, swap pairs (quad_perm), then mirror within 8 and within
-// 16 lanes.  Every step adds two values that the partner lane adds in the
-// other order, and FP32 addition is commutative, so all 16 lanes end with
-// the same bits.
-__device__ __forceinline__ float row16_sum(float v) {
+// Sum over the kLanes lanes of a row, the result in all of them.  Steps:
+// swap neighbours, swap pairs (quad_perm), mirror within 8 lanes, mirror
+// within 16 lanes (DPP), then swaps with the lane 16 and 32 away.  Every
+// step adds two values that the partner lane adds in the other order, and
+// FP32 addition is commutative, so all lanes of a row end with the same
+// bits.  Every lane of the wave must be active.
+template <int kLanes>
+__device__ __forceinline__ float row_sum(float v) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
+  if constexpr (kLanes >= 16) v += dpp_mov<0x140>(v);  // row_mirror
+  if constexpr (kLanes >= 32) v += __shfl_xor(v, 16);
+  if constexpr (kLanes >= 64) v += __shfl_xor(v, 32);
   return v;
 }
 

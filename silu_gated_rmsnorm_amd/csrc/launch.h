@@ -10,37 +10,48 @@ namespace grn {
 
 // Rows per dw chunk.  The backward adds the dw contributions of chunk
 // [c*R, (c+1)*R) into one FP32 partial, one workgroup per chunk; R, and
-// therefore the bits of dw, depend only on the number of rows.  One size
-// serves all row counts: smaller chunks for small problems (32 or 64 rows
-// below 196,608 rows) measured slower on MI355X, because the extra partials
-// and hand-offs cost more than the added parallelism gains.
+// therefore the bits of dw, depend only on the row size.  R = 128 rows
+// serves every row count (smaller chunks for small problems, 32 or 64 rows,
+// measured slower on MI355X: the extra partials and hand-offs cost more
+// than the added parallelism gains).  Rows of 128 bytes (D = 64 in a 16-bit
+// type) take 256-row chunks, so that a chunk's fixed cost is spread over as
+// many bytes (measured at 7684x48: 54 -> 48 us; 256-byte FP32 rows of
+// D = 64 were faster with 128-row chunks).
 #ifndef GRN_CHUNK_ROWS
 #define GRN_CHUNK_ROWS 128
 #endif
 constexpr int kChunkRows = GRN_CHUNK_ROWS;
 
-constexpr int chunk_rows_for(int64_t /*rows*/) { return kChunkRows; }
+constexpr int chunk_rows_for(int32_t row_bytes) {
+  return row_bytes <= 128 ? 2 * kChunkRows : kChunkRows;
+}
 
 // Workspace of the backward, in this order:
 //   counters  uint32[kCounterWords]  arrival counters (zero between calls)
-//   partial   float[nchunks][128]     one dw partial per chunk
-//   gpart     float[ngroups][128]     one dw partial per group of chunks
-// The counter region holds, as 32-bit words:
-//   [0, ngroups)                 one arrival counter per group (ngroups is at
+//   partial   float[nchunks][D]       one dw partial per chunk
+//   gpart     float[ngroups][D]       one dw partial per group of chunks
+// The counter region holds:
+//   words [0, ngroups)           one arrival counter per group (ngroups is at
 //                                most 4096: ceil(sqrt(nchunks)) <= 4096 for
 //                                nchunks <= 2^24, i.e. rows < 2^31)
-//   [kNondetAccum, +slots*128)   the FP32 accumulators of the
-//                                non-deterministic dw, kNondetSlots of them
-//   [kMaxGroups]                 the overall counter
+//   bytes [kNondetAccumByte, +nondet_slots(D)*8*D)
+//                                the FP64 accumulators of the
+//                                non-deterministic dw
+//   word  kMaxGroups             the overall counter
 constexpr int kMaxGroups = 8191;
 constexpr int kCounterWords = kMaxGroups + 1;
 #ifndef GRN_NONDET_SLOTS
 #define GRN_NONDET_SLOTS 16
 #endif
-constexpr int kNondetSlots = GRN_NONDET_SLOTS;
-constexpr int kNondetAccum = 4096;
-static_assert(kNondetSlots >= 1 && kNondetAccum + kNondetSlots * 128 <= kMaxGroups,
-              "the non-deterministic accumulators must fit the counter region");
+constexpr int kNondetAccumByte = 4096 * 4;
+// Accumulators of D doubles each that fit below the overall counter (16 for
+// D = 64, 15 for D = 128, 7 for D = 256).
+constexpr int nondet_slots(int D) {
+  return (kMaxGroups * 4 - kNondetAccumByte) / (8 * D) < GRN_NONDET_SLOTS
+             ? (kMaxGroups * 4 - kNondetAccumByte) / (8 * D)
+             : GRN_NONDET_SLOTS;
+}
+static_assert(nondet_slots(256) >= 1, "the non-deterministic accumulators fit");
 constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
 
 struct BwdLayout {
@@ -53,24 +64,29 @@ struct BwdLayout {
   size_t bytes = 0;
 };
 
-BwdLayout bwd_layout(int64_t rows);
+// Exact layout for rows of D values of `esize` bytes.  esize = 0 gives the
+// largest layout over the element types (the size to allocate when the type
+// is not known).
+BwdLayout bwd_layout(int64_t rows, int32_t D, int32_t esize);
 
-// Row strides of the activations, in elements (each a multiple of 8, i.e.
-// 16-byte rows, and at most kMaxStride).  Packed rows have stride 128.
+// Row strides of the activations, in elements (each keeps rows 16-byte
+// aligned: a multiple of 8 for 16-bit types, of 4 for FP32; at most
+// kMaxStride).  Packed rows have stride D.
 struct RowStrides {
-  int64_t x = 128, g = 128, y = 128, dy = 128, dx = 128, dg = 128;
+  int64_t x = 0, g = 0, y = 0, dy = 0, dx = 0, dg = 0;
 };
 constexpr int64_t kMaxStride = int64_t{1} << 24;
 
+// dtype: 0 BF16, 1 FP16, 2 FP32 (GRN_DTYPE_*); D: 64, 128 or 256.
 hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
-                      const RowStrides& st, int64_t rows, float eps, int max_wg,
-                      hipStream_t s);
+                      const RowStrides& st, int64_t rows, int32_t D, int32_t dtype,
+                      float eps, int max_wg, hipStream_t s);
 
 hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
                       int dw_fp32, int deterministic, void* workspace,
-                      const RowStrides& st, int64_t rows, float eps, int max_wg,
-                      hipStream_t s);
+                      const RowStrides& st, int64_t rows, int32_t D, int32_t dtype,
+                      float eps, int max_wg, hipStream_t s);
 
 hipError_t launch_counters_zero(void* workspace, hipStream_t s);
 

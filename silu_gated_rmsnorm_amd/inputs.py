@@ -13,7 +13,8 @@ then w = 1 + 0.1 * N(0, 1) of shape ``[D]``, then (only when
 ``outlier_frac > 0``) a permutation of the rows whose first
 ``int(rows * outlier_frac)`` entries select outlier rows of x, which are
 multiplied by ``outlier_scale``.  All draws are float32 and are rounded to
-BF16 (round to nearest even) once, at the end.  The same seed gives
+the storage type (BF16 by default; FP16 or FP32 on request; round to
+nearest even) once, at the end.  The same seed gives
 different numbers on the CPU and on the GPU (different generators); each
 test hands the very same bytes to both sides.
 """
@@ -42,9 +43,10 @@ class Workload:
         return self.T * self.H
 
 
-# The five shapes the benchmark and the parity tests use (all D = 128,
-# eps = 1e-6, seed 0).  1031x48 and 7684x48 appear in Table 2 of PR #8701;
-# the larger three extend the same T x 48 family.
+# The shapes the benchmark and the parity tests use (all D = 128,
+# eps = 1e-6, seed 0).  1031x48 and 7684x48 appear in Table 2 of PR #8701
+# and 16384x32 (the H = 32 head count) in its Tables 1 and 2; the larger
+# three T x 48 shapes extend the same family.
 WORKLOADS = {
     "1031x48": Workload("1031x48", 1031, 48),
     "7684x48": Workload("7684x48", 7684, 48),
@@ -52,13 +54,15 @@ WORKLOADS = {
     "65536x48": Workload("65536x48", 65536, 48),
     "262144x48_outliers": Workload("262144x48_outliers", 262144, 48,
                                    g_std=2.0, outlier_frac=0.01),
+    "16384x32": Workload("16384x32", 16384, 32),
 }
 
 
 def make_inputs(rows: int, D: int = 128, *, seed: int = 0,
                 device="cpu", g_std: float = 1.0,
-                outlier_frac: float = 0.0, outlier_scale: float = 100.0):
-    """Return ``dict(x, g, dy, w)`` of BF16 tensors on ``device``."""
+                outlier_frac: float = 0.0, outlier_scale: float = 100.0,
+                dtype=torch.bfloat16):
+    """Return ``dict(x, g, dy, w)`` of ``dtype`` tensors on ``device``."""
     device = torch.device(device)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -78,18 +82,19 @@ def make_inputs(rows: int, D: int = 128, *, seed: int = 0,
         sel = perm[: int(rows * outlier_frac)]
         x[sel] *= outlier_scale
     return {
-        "x": x.to(torch.bfloat16),
-        "g": g.to(torch.bfloat16),
-        "dy": dy.to(torch.bfloat16),
-        "w": w.to(torch.bfloat16),
+        "x": x.to(dtype),
+        "g": g.to(dtype),
+        "dy": dy.to(dtype),
+        "w": w.to(dtype),
     }
 
 
-def make_workload_inputs(wl: Workload, *, seed: int = 0, device="cpu"):
+def make_workload_inputs(wl: Workload, *, seed: int = 0, device="cpu",
+                         dtype=torch.bfloat16):
     """``make_inputs`` with the distributions of a named workload."""
     return make_inputs(wl.rows, wl.D, seed=seed, device=device,
                        g_std=wl.g_std, outlier_frac=wl.outlier_frac,
-                       outlier_scale=wl.outlier_scale)
+                       outlier_scale=wl.outlier_scale, dtype=dtype)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

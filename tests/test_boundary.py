@@ -28,7 +28,7 @@ def addr(k):
 
 
 X, G, W, DY, Y, DX, DG, DW, WS = (addr(k) for k in range(9))
-WS_BYTES = 32768 + 512 + 512    # counters + 1 chunk partial + 1 group partial (10 rows)
+WS_BYTES = 32768 + 2048         # counters + chunk and group partials (10 rows, D <= 256)
 
 
 def declared_functions():
@@ -53,25 +53,35 @@ def test_header_symbols_exported(lib):
 def test_workspace_bytes(lib):
     C = lib.gated_rmsnorm_workspace_init_bytes()
     assert C == 32768
-    assert lib.gated_rmsnorm_chunk_rows(0) == 0
+    assert lib.gated_rmsnorm_chunk_rows(0, 128, 0) == 0
+    assert lib.gated_rmsnorm_chunk_rows(10, 96, 0) == 0
+    assert lib.gated_rmsnorm_chunk_rows(10, 128, 3) == 0
     for rows in (1, 49488, 196608, 12582912):
-        assert lib.gated_rmsnorm_chunk_rows(rows) == 128
+        for dt in (0, 1, 2):
+            assert lib.gated_rmsnorm_chunk_rows(rows, 128, dt) == 128
+            assert lib.gated_rmsnorm_chunk_rows(rows, 256, dt) == 128
+        # 128-byte rows (D = 64, 16-bit) take 256-row chunks
+        assert lib.gated_rmsnorm_chunk_rows(rows, 64, 0) == 256
+        assert lib.gated_rmsnorm_chunk_rows(rows, 64, 1) == 256
+        assert lib.gated_rmsnorm_chunk_rows(rows, 64, 2) == 128
 
-    def expect(rows):
-        R = lib.gated_rmsnorm_chunk_rows(rows)
+    def expect(rows, D=128):
+        R = 128   # the size allocated covers the smallest chunks of any type
         chunks = math.ceil(rows / R)
         gs = math.isqrt(chunks - 1) + 1 if chunks > 1 else 1   # ceil(sqrt(chunks))
-        return C + (chunks + math.ceil(chunks / gs)) * 512
+        return C + (chunks + math.ceil(chunks / gs)) * 4 * D
 
     assert lib.gated_rmsnorm_workspace_bytes(0, 128) == 0
     assert lib.gated_rmsnorm_workspace_bytes(-5, 128) == 0
-    assert lib.gated_rmsnorm_workspace_bytes(10, 64) == 0
+    for bad_d in (0, 32, 96, 127, 192, 512):
+        assert lib.gated_rmsnorm_workspace_bytes(10, bad_d) == 0
     assert lib.gated_rmsnorm_workspace_bytes(1, 128) == C + 1024
     assert lib.gated_rmsnorm_workspace_bytes(128, 128) == C + 1024
     assert lib.gated_rmsnorm_workspace_bytes(129, 128) == C + 3 * 512
     for rows in (5 * 128, 17 * 128 + 3, 49488, 196607, 196608, 368832, 1572864, 12582912,
                  2**31 - 1):
-        assert lib.gated_rmsnorm_workspace_bytes(rows, 128) == expect(rows), rows
+        for D in (64, 128, 256):
+            assert lib.gated_rmsnorm_workspace_bytes(rows, D) == expect(rows, D), (rows, D)
     assert lib.gated_rmsnorm_workspace_bytes(2**31, 128) == 0
 
 
@@ -92,6 +102,19 @@ def bwd(lib, x=X, g=G, w=W, dy=DY, dx=DX, dg=DG, dw=DW, ws=WS, ws_bytes=WS_BYTES
                                  eps, dtype, dw_fp32, None)
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=0), SHAPE), (dict(D=32), SHAPE), (dict(D=127), SHAPE), (dict(D=512), SHAPE),
+    (dict(rows=-1), SHAPE), (dict(rows=2**31), SHAPE), (dict(dtype=-1), DTYPE),
+    (dict(dtype=3), DTYPE), (dict(eps=float("nan")), EPS), (dict(x=None), NULL),
+    (dict(w=None), NULL), (dict(y=X), ALIAS), (dict(y=W), ALIAS), (dict(y=G + 16), ALIAS),
+    (dict(x=X + 8), ALIGN), (dict(w=W + 4, dtype=2), ALIGN),
+    # a [10, 256] FP32 y 10 KiB long reaches into x placed 8 KiB after it
+    (dict(D=256, dtype=2, y=X - 8192), ALIAS),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
 def ckpt(lib, y=Y, **kw):
     a = dict(x=X, g=G, w=W, dy=DY, dx=DX, dg=DG, dw=DW, ws=WS, ws_bytes=WS_BYTES,
              rows=ROWS, D=128, eps=1e-6, dtype=0, dw_fp32=1)
@@ -103,13 +126,17 @@ def ckpt(lib, y=Y, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(D=256), SHAPE), (dict(dtype=3), DTYPE), (dict(dw_fp32=2), DTYPE),
+    (dict(D=192), SHAPE), (dict(D=512), SHAPE), (dict(dtype=3), DTYPE), (dict(dw_fp32=2), DTYPE),
     (dict(dw_fp32=-1), DTYPE), (dict(eps=-0.5), EPS),
     (dict(ws_bytes=0), WORKSPACE), (dict(ws_bytes=511), WORKSPACE),
     (dict(ws=None), WORKSPACE),
     (dict(dy=None), NULL), (dict(dx=None), NULL), (dict(dg=None), NULL), (dict(dw=None), NULL),
     (dict(dy=DY + 8), ALIGN), (dict(dw=DW + 2, dw_fp32=1), ALIGN), (dict(dw=DW + 1, dw_fp32=0), ALIGN),
     (dict(ws=WS + 4), ALIGN),
+    # FP32 dw of FP16 inputs, FP32 dw of FP32 inputs: 4-byte aligned
+    (dict(dtype=1, dw=DW + 2, dw_fp32=1), ALIGN), (dict(dtype=2, dw=DW + 2, dw_fp32=0), ALIGN),
+    (dict(dtype=1, dw=DW + 1, dw_fp32=0), ALIGN),
+    (dict(D=64, ws_bytes=32768 + 511), WORKSPACE), (dict(D=256, ws_bytes=32768 + 2047), WORKSPACE),
     (dict(dx=X), ALIAS), (dict(dx=DY + 32), ALIAS), (dict(dg=DX), ALIAS),
     (dict(dw=DX + 64), ALIAS), (dict(ws=DG + 256), ALIAS), (dict(dw=WS + 128), ALIAS),
     (dict(dw=W), ALIAS),
@@ -127,8 +154,9 @@ def test_ckpt_rejects(lib, kw, code):
     assert ckpt(lib, **kw) == code
 
 
-def fwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, y=Y, sy=128, rows=ROWS, D=128, eps=1e-6):
-    return lib.gated_rmsnorm_fwd_strided(x, sx, g, sg, w, y, sy, rows, D, eps, 0, None)
+def fwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, y=Y, sy=128, rows=ROWS, D=128, eps=1e-6,
+          dtype=0):
+    return lib.gated_rmsnorm_fwd_strided(x, sx, g, sg, w, y, sy, rows, D, eps, dtype, None)
 
 
 def bwd_s(lib, x=X, sx=128, g=G, sg=128, w=W, dy=DY, sdy=128, dx=DX, sdx=128, dg=DG,
@@ -151,6 +179,11 @@ def ckpt_s(lib, det=1, dw_fp32=1, y=Y):
     (dict(sx=256, sy=256, y=X + 240), ALIAS),
     # y overlapping g with a different pitch (conservative range test)
     (dict(sg=256, sy=384, y=G + 256), ALIAS),
+    # rows stay 16-byte aligned: 4-element steps for FP32, 8 for FP16
+    (dict(dtype=2, sx=130), ALIGN), (dict(dtype=1, sg=132), ALIGN), (dict(D=64, sy=60), SHAPE),
+    (dict(D=256, sx=248), SHAPE),
+    # FP32 rows of 512 bytes: y at x + 256 bytes shares half of each row of x
+    (dict(dtype=2, sx=256, sy=256, y=X + 256), ALIAS),
 ])
 def test_fwd_strided_rejects(lib, kw, code):
     assert fwd_s(lib, **kw) == code

@@ -233,7 +233,7 @@ def test_rows_independent_and_dw_order_free():
 # library routines: torch autograd in float64
 
 @pytest.mark.parametrize("eps", [1e-6, 1e-2])
-@pytest.mark.parametrize("D", [1, 8, 128])
+@pytest.mark.parametrize("D", [1, 8, 64, 128, 256])
 def test_against_torch_autograd_fp64(eps, D):
     rows = 9
     x = _rand(rows, D, 30) * np.linspace(0.1, 10, rows)[:, None]
@@ -278,8 +278,8 @@ def _fd(arr, f):
     return out
 
 
-@pytest.mark.parametrize("rows", [1, 3])
-@pytest.mark.parametrize("D", [1, 2, 8, 16, 128])
+@pytest.mark.parametrize("rows,D", [(r, d) for r in (1, 3) for d in (1, 2, 8, 16, 128)]
+                         + [(1, 64), (1, 256)])
 @pytest.mark.parametrize("eps", [1e-6, 1e-2])
 def test_finite_differences(rows, D, eps):
     rng = np.random.default_rng(1000 * rows + D)
