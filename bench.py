@@ -57,7 +57,7 @@ COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
 # steps, deterministic).
-BWD_KERNEL = "grn::bwd_kernel<Dt::{dtype}, {D}, 4, 4, 128, 1, true>"
+BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, 4, 4, {R}, 1, true>"
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 
@@ -348,7 +348,8 @@ def main():
         # (rows > 0), timed over back-to-back launches on its stream.
         per_launch = bwd_bytes
         achieved = per_launch / (bwd_us * 1e-6) / 1e9
-        roofline = {"kernel": BWD_KERNEL.format(dtype=args.dtype, D=D), "bound": "hbm",
+        kname = BWD_KERNEL.format(code=dt_code, D=D, R=256 if row_bytes <= 128 else 128)
+        roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic_from_counters() if default_shape else None,
