@@ -286,7 +286,8 @@ def main():
                  "bwdg_f32": (lambda st: op_bwd(st, True), bwd32_bytes),
                  "bwdg_nondet_f32": (lambda st: op_bwd(st, True, False), bwd32_bytes),
                  "ckptg": (op_ckpt, ckpt_bytes),
-                 "stepg_f32": (lambda st: op_ckpt(st, True), ckpt32_bytes)}
+                 "stepg_f32": (lambda st: op_ckpt(st, True), ckpt32_bytes),
+                 "stepg": (op_step, step_bytes)}
         for name, (fn, nbytes) in kinds.items():
             graphs = []
             for st in sets:
