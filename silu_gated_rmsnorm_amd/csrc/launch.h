@@ -31,14 +31,17 @@ constexpr int chunk_rows_for(int32_t row_bytes) {
 //   partial   float[nchunks][D]       one dw partial per chunk
 //   gpart     float[ngroups][D]       one dw partial per group of chunks
 // The counter region holds:
-//   words [0, ngroups)           one arrival counter per group (ngroups is at
-//                                most 4096: ceil(sqrt(nchunks)) <= 4096 for
+//   words [0, 4096)              one arrival counter per group, group g at
+//                                word g * counter_stride (ngroups is at most
+//                                4096: ceil(sqrt(nchunks)) <= 4096 for
 //                                nchunks <= 2^24, i.e. rows < 2^31)
 //   bytes [kNondetAccumByte, +nondet_slots(D)*8*D)
 //                                the FP64 accumulators of the
 //                                non-deterministic dw
 //   word  kMaxGroups             the overall counter
 constexpr int kMaxGroups = 8191;
+constexpr int kGroupCounterWords = 4096;
+constexpr int kMaxCounterStride = 64;  // 256 bytes: counters on separate lines
 constexpr int kCounterWords = kMaxGroups + 1;
 #ifndef GRN_NONDET_SLOTS
 #define GRN_NONDET_SLOTS 16
@@ -59,6 +62,7 @@ struct BwdLayout {
   int64_t nchunks = 0;
   int64_t group_size = 1;
   int64_t ngroups = 0;
+  int64_t counter_stride = 1;  // words between group counters (a power of 2)
   size_t partial_off = 0;
   size_t gpart_off = 0;
   size_t bytes = 0;
