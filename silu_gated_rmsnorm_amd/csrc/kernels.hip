@@ -526,7 +526,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
         }
         __syncthreads();
         if (t == 0)
-          last_overall = __hip_atomic_fetch_add(&counters[kMaxGroups], 1u, __ATOMIC_RELAXED,
+          last_overall = __hip_atomic_fetch_add(&counters[kOverallCounter], 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT) ==
                          (uint32_t)(nchunks - 1);
         __syncthreads();
@@ -547,7 +547,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
                                  __HIP_MEMORY_SCOPE_AGENT);
           }
           if (t == 0)
-            __hip_atomic_store(&counters[kMaxGroups], 0u, __ATOMIC_RELAXED,
+            __hip_atomic_store(&counters[kOverallCounter], 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
@@ -581,7 +581,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
       __syncthreads();
       // Level 3: the workgroup that completes the last group sums them all.
       if (t == 0)
-        last_overall = __hip_atomic_fetch_add(&counters[kMaxGroups], 1u, __ATOMIC_RELAXED,
+        last_overall = __hip_atomic_fetch_add(&counters[kOverallCounter], 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT) ==
                        (uint32_t)(ngroups - 1);
       __syncthreads();
@@ -589,7 +589,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
         const float total = column_sum_fixed<kThreads, D>(gpart, ngroups, lds);
         if (t < D) store_dw<T>(dw, dw_fp32, t, total);
         if (t == 0)
-          __hip_atomic_store(&counters[kMaxGroups], 0u, __ATOMIC_RELAXED,
+          __hip_atomic_store(&counters[kOverallCounter], 0u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }

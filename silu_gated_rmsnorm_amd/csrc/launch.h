@@ -31,27 +31,34 @@ constexpr int chunk_rows_for(int32_t row_bytes) {
 //   partial   float[nchunks][D]       one dw partial per chunk
 //   gpart     float[ngroups][D]       one dw partial per group of chunks
 // The counter region holds:
-//   words [0, 4096)              one arrival counter per group, group g at
-//                                word g * counter_stride (ngroups is at most
-//                                4096: ceil(sqrt(nchunks)) <= 4096 for
-//                                nchunks <= 2^24, i.e. rows < 2^31)
+//   words [0, kGroupCounterWords)  one arrival counter per group, group g
+//                                  at word g * counter_stride (ngroups is at
+//                                  most 4096: ceil(sqrt(nchunks)) <= 4096
+//                                  for nchunks <= 2^24, i.e. rows < 2^31)
 //   bytes [kNondetAccumByte, +nondet_slots(D)*8*D)
-//                                the FP64 accumulators of the
-//                                non-deterministic dw
-//   word  kMaxGroups             the overall counter
-constexpr int kMaxGroups = 8191;
-constexpr int kGroupCounterWords = 4096;
-constexpr int kMaxCounterStride = 64;  // 256 bytes: counters on separate lines
-constexpr int kCounterWords = kMaxGroups + 1;
+//                                  the FP64 accumulators of the
+//                                  non-deterministic dw
+//   word  kOverallCounter          the overall counter (the last word)
+#ifndef GRN_COUNTER_WORDS
+#define GRN_COUNTER_WORDS 8192
+#endif
+#ifndef GRN_MAX_COUNTER_STRIDE
+#define GRN_MAX_COUNTER_STRIDE 64
+#endif
+constexpr int kCounterWords = GRN_COUNTER_WORDS;
+constexpr int kOverallCounter = kCounterWords - 1;
+constexpr int kGroupCounterWords = kCounterWords / 2;
+constexpr int kMaxCounterStride = GRN_MAX_COUNTER_STRIDE;  // 64: counters 256 B apart
+static_assert(kGroupCounterWords >= 4096, "one counter word per group at least");
 #ifndef GRN_NONDET_SLOTS
 #define GRN_NONDET_SLOTS 16
 #endif
-constexpr int kNondetAccumByte = 4096 * 4;
+constexpr int kNondetAccumByte = kGroupCounterWords * 4;
 // Accumulators of D doubles each that fit below the overall counter (16 for
 // D = 64, 15 for D = 128, 7 for D = 256).
 constexpr int nondet_slots(int D) {
-  return (kMaxGroups * 4 - kNondetAccumByte) / (8 * D) < GRN_NONDET_SLOTS
-             ? (kMaxGroups * 4 - kNondetAccumByte) / (8 * D)
+  return (kOverallCounter * 4 - kNondetAccumByte) / (8 * D) < GRN_NONDET_SLOTS
+             ? (kOverallCounter * 4 - kNondetAccumByte) / (8 * D)
              : GRN_NONDET_SLOTS;
 }
 static_assert(nondet_slots(256) >= 1, "the non-deterministic accumulators fit");
