@@ -88,23 +88,26 @@ def test_ckpt_step_equals_fwd_then_bwd(dw_fp32):
 
 def test_workspace_reused_across_sizes():
     """The counters return to zero after each call: one workspace serves
-    calls of different sizes in any order, with the same bits as fresh ones."""
-    big, small = 200000, 3001
-    say(f"[determinism] workspace reuse rows={big},{small}")
-    a = make_inputs(big, seed=9, device="cuda")
-    b = make_inputs(small, seed=10, device="cuda")
-    need = max(binding.gated_rmsnorm_workspace_bytes(r) for r in (big, small))
+    calls of different sizes in any order, with the same bits as fresh ones.
+    The sizes give 40, 5 and 115 groups, i.e. different spacings of the
+    group counters (64, 64 and 32 words)."""
+    sizes = (200000, 3001, 1700000)
+    say(f"[determinism] workspace reuse rows={sizes}")
+    inps = [make_inputs(r, seed=9 + k, device="cuda") for k, r in enumerate(sizes)]
+    need = max(binding.gated_rmsnorm_workspace_bytes(r) for r in sizes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    order = (0, 1, 2, 0, 1, 1, 2, 2, 0)
     outs = []
-    for inp in (a, b, a, b, b, a):
+    for k in order:
+        inp = inps[k]
         outs.append(binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], 1e-6,
                                               dw_fp32=True, workspace=ws))
     torch.cuda.synchronize()
-    fresh_a = binding.gated_rmsnorm_bwd(a["x"], a["g"], a["w"], a["dy"], 1e-6, dw_fp32=True)
-    fresh_b = binding.gated_rmsnorm_bwd(b["x"], b["g"], b["w"], b["dy"], 1e-6, dw_fp32=True)
+    fresh = [binding.gated_rmsnorm_bwd(i["x"], i["g"], i["w"], i["dy"], 1e-6, dw_fp32=True)
+             for i in inps]
     torch.cuda.synchronize()
-    for out, ref in zip(outs, (fresh_a, fresh_b, fresh_a, fresh_b, fresh_b, fresh_a)):
-        for x, y in zip(out, ref):
+    for out, k in zip(outs, order):
+        for x, y in zip(out, fresh[k]):
             assert _same(x, y)
     C = binding.load_library().gated_rmsnorm_workspace_init_bytes()
     assert torch.count_nonzero(ws[:C]).item() == 0
