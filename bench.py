@@ -361,8 +361,8 @@ def main():
         cpu = cpu_baseline(inp, wl, fwd_bytes + bwd_bytes, args.cpu_seconds)
 
     out = {
-        "metric": "achieved HBM GB/s (% of peak) + us, gated RMSNorm fwd/bwd at "
-                  f"{wl.name}x{D} {args.dtype}",
+        "metric": "achieved HBM GB/s (% of peak) + \u00b5s, gated RMSNorm fwd/bwd at "
+                  f"{wl.T}x{wl.H}x{D} {args.dtype}",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,

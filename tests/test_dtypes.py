@@ -130,3 +130,28 @@ def test_16384x32_full_size():
     b = {k: bits(v) for k, v in inp.items()}
     _, _, dw_ref = oracle.bwd(b["x"], b["g"], b["w"], b["dy"], wl.eps)
     _check_dw(dw, dw_ref, torch.bfloat16, True)
+
+
+def test_f16_outputs_beyond_range_are_infinite():
+    """FP16 storage: a y whose exact value lies beyond FP16's range (>= 65520
+    after rounding) comes out infinite with the right sign, the rest of the
+    row stays finite and within the bar."""
+    rows, D = 4, 128
+    say(f"[dtypes] f16 overflow rows={rows}")
+    inp = make_inputs(rows, D, seed=77, device="cuda", dtype=torch.float16)
+    g = inp["g"].clone()
+    w = inp["w"].clone()
+    g[0, :8] = 400.0       # silu(400) = 400
+    w[:8] = 300.0          # |y| ~ |n| * 1.2e5 for the first 8 columns of row 0
+    inp = {"x": inp["x"], "g": g, "w": w, "dy": inp["dy"]}
+    y = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
+    torch.cuda.synchronize()
+    y_ref, _, _, _ = _oracle(inp, 1e-6)
+    got = _f64(y)
+    big = np.abs(y_ref) >= 65520.0
+    assert big.any()
+    assert np.all(np.isinf(got[big])) and np.all(np.sign(got[big]) == np.sign(y_ref[big]))
+    rest = ~big
+    assert np.all(np.isfinite(got[rest]))
+    err = np.max(np.abs(got[rest] - y_ref[rest]) / np.maximum(np.abs(y_ref[rest]), 1e-3))
+    assert err <= Y_TOL_F16, err
