@@ -126,3 +126,18 @@ def test_nondefault_stream():
     s.synchronize()
     for a, b in zip(ref, out):
         assert _same(a, b)
+
+
+def test_forward_tile_size_invariance():
+    """The forward picks a larger tile for tensors of 128 MiB and more; a
+    row's y must not depend on it: rows of a large call equal the same rows
+    computed in a small call, bit for bit."""
+    rows = 600000   # 153.6 MB per BF16 tensor: the large-tile path
+    say(f"[determinism] forward tile size rows={rows}")
+    inp = make_inputs(rows, seed=12, device="cuda")
+    y_big = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
+    for lo, hi in ((0, 4099), (rows - 3001, rows), (250000, 260003)):
+        y_small = binding.gated_rmsnorm_fwd(inp["x"][lo:hi].contiguous(),
+                                            inp["g"][lo:hi].contiguous(), inp["w"], 1e-6)
+        torch.cuda.synchronize()
+        assert _same(y_big[lo:hi].contiguous(), y_small)
