@@ -57,7 +57,7 @@ COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
 # steps, deterministic).
-BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, 4, 4, {R}, 1, true>"
+BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true>"
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 
@@ -349,7 +349,12 @@ def main():
         # (rows > 0), timed over back-to-back launches on its stream.
         per_launch = bwd_bytes
         achieved = per_launch / (bwd_us * 1e-6) / 1e9
-        kname = BWD_KERNEL.format(code=dt_code, D=D, R=256 if row_bytes <= 128 else 128)
+        # The library picks the backward's shape by tensor size (32 MiB and
+        # 256 MiB boundaries): row groups per wave step and prefetched steps.
+        tb = rows * row_bytes
+        u, pf = (2, 1) if tb < (32 << 20) else ((4, 0) if tb < (256 << 20) else (4, 1))
+        kname = BWD_KERNEL.format(code=dt_code, D=D, U=u, R=256 if row_bytes <= 128 else 128,
+                                  PF=pf)
         roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),

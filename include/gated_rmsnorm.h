@@ -133,9 +133,9 @@ grn_status gated_rmsnorm_fwd(const void *x, const void *g, const void *w,
  *      zero (see the workspace contract above; may be NULL when rows = 0).
  * Out: dx, dg [rows, D] of type dtype; dw [D], FP32 if dw_fp32 = 1, else
  *      of type dtype.
- * dw is summed in FP32 in a fixed order that depends only on rows (per
- * chunk of rows, then per group of chunks, then over groups): it is
- * bit-identical from run to run and across launch shapes.  The whole
+ * dw is summed in FP32 in a fixed order that depends only on rows, D and
+ * dtype (per chunk of rows, then per group of chunks, then over groups): it
+ * is bit-identical from run to run and across launch shapes.  The whole
  * backward is one kernel launch (two dependent kernels never run). */
 grn_status gated_rmsnorm_bwd(const void *x, const void *g, const void *w,
                              const void *dy, void *dx, void *dg, void *dw,

@@ -36,8 +36,36 @@
 #ifndef GRN_FWD_LARGE_BYTES
 #define GRN_FWD_LARGE_BYTES (128ll << 20)
 #endif
-#ifndef GRN_BWD_U
-#define GRN_BWD_U 4          // row groups per wave step in the backward
+// Backward shape by tensor size (bytes of one [rows, D] activation):
+// row groups per wave step (U) and steps of loads prefetched ahead (PF).
+// U changes the order in which a chunk's rows are added into dw, so dw's
+// bits depend on the tier, which depends only on rows, D and the type.
+#ifndef GRN_BWD_SMALL_BYTES
+#define GRN_BWD_SMALL_BYTES (32ll << 20)
+#endif
+#ifndef GRN_BWD_LARGE_BYTES
+#define GRN_BWD_LARGE_BYTES (256ll << 20)
+#endif
+#ifndef GRN_BWD_U_SMALL
+#define GRN_BWD_U_SMALL 2
+#endif
+#ifndef GRN_BWD_PF_SMALL
+#define GRN_BWD_PF_SMALL 1
+#endif
+#ifndef GRN_BWD_U_MID
+#define GRN_BWD_U_MID 4
+#endif
+#ifndef GRN_BWD_PF_MID
+#define GRN_BWD_PF_MID 0
+#endif
+#ifndef GRN_BWD_U_LARGE
+#define GRN_BWD_U_LARGE 4
+#endif
+#ifndef GRN_BWD_PF_LARGE
+#define GRN_BWD_PF_LARGE 1
+#endif
+#ifndef GRN_BWD_U_ND
+#define GRN_BWD_U_ND 4       // the non-deterministic dw kernel, all sizes
 #endif
 #ifndef GRN_BWD_WAVES
 #define GRN_BWD_WAVES 4      // waves per backward workgroup
@@ -45,11 +73,8 @@
 #ifndef GRN_BWD_MIN_WAVES
 #define GRN_BWD_MIN_WAVES 0  // >0: ask for at least this many waves per SIMD
 #endif
-#ifndef GRN_BWD_PREFETCH
-#define GRN_BWD_PREFETCH 1   // steps of loads kept in flight ahead of the one
-#endif                       // being computed (0 = none), deterministic dw
 #ifndef GRN_BWD_ND_PREFETCH
-#define GRN_BWD_ND_PREFETCH 0  // the same for the non-deterministic dw kernel
+#define GRN_BWD_ND_PREFETCH 0  // steps prefetched by the non-deterministic kernel
 #endif
 #ifndef GRN_SUM_BATCH
 #define GRN_SUM_BATCH 8      // partial rows per thread per round trip in the dw tree
@@ -736,6 +761,7 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                     (uint32_t)(st.dy / vec), (uint32_t)(st.dx / vec),
                     (uint32_t)(st.dg / vec)};
   char* ws = static_cast<char*>(workspace);
+  const int64_t tensor_bytes = rows * (int64_t)D * (16 / vec);
   const int64_t nwork = L.nchunks + (deterministic && kReducers ? L.ngroups : 0);
   const int64_t grid = cap_grid(nwork, max_wg);
   return with_shape(dtype, D, [&](auto tt, auto dd) {
@@ -756,12 +782,16 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                          reinterpret_cast<uint32_t*>(ws), dw, dw_fp32, rows, eps,
                          L.nchunks, L.group_size, L.ngroups, L.counter_stride);
     };
-    // Each of the two kernels has its own prefetch depth: the one measured
-    // fastest for it (their register budgets differ).
-    if (deterministic) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U, kBwdWaves, kR, GRN_BWD_PREFETCH, true>);
+    // Shapes measured fastest per size (7684x48 and 16384x32 are "mid",
+    // 1031x48 "small", 32768x48 and up "large").
+    if (!deterministic) {
+      launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false>);
+    } else if (tensor_bytes < GRN_BWD_SMALL_BYTES) {
+      launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true>);
+    } else if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
+      launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true>);
     } else {
-      launch(bwd_kernel<T, DD, GRN_BWD_U, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true>);
     }
     return hipGetLastError();
   });
