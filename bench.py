@@ -56,8 +56,8 @@ R200_7684x48_US = {
 COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
-# steps, deterministic).
-BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true>"
+# steps, deterministic, last step's stores held back).
+BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}>"
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 
@@ -350,11 +350,13 @@ def main():
         per_launch = bwd_bytes
         achieved = per_launch / (bwd_us * 1e-6) / 1e9
         # The library picks the backward's shape by tensor size (32 MiB and
-        # 256 MiB boundaries): row groups per wave step and prefetched steps.
+        # 256 MiB boundaries): row groups per wave step, prefetched steps and
+        # (large tensors of FP32, or BF16 up to D = 128) held stores.
         tb = rows * row_bytes
         u, pf = (2, 1) if tb < (32 << 20) else ((4, 0) if tb < (256 << 20) else (4, 1))
+        hold = tb >= (256 << 20) and (args.dtype == "f32" or (args.dtype == "bf16" and D <= 128))
         kname = BWD_KERNEL.format(code=dt_code, D=D, U=u, R=256 if row_bytes <= 128 else 128,
-                                  PF=pf)
+                                  PF=pf, HOLD="true" if hold else "false")
         roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),

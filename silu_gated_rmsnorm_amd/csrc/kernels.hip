@@ -64,6 +64,11 @@
 #ifndef GRN_BWD_PF_LARGE
 #define GRN_BWD_PF_LARGE 1
 #endif
+// Large tensors: hold the dx/dg stores of a chunk's last step until after
+// the wait for the chunk's dw partial (see bwd_kernel; hold_large()).
+#ifndef GRN_BWD_HOLD_LARGE
+#define GRN_BWD_HOLD_LARGE 1
+#endif
 #ifndef GRN_BWD_U_ND
 #define GRN_BWD_U_ND 4       // the non-deterministic dw kernel, all sizes
 #endif
@@ -231,6 +236,16 @@ struct BwdRaw {
   u32x4 x[U], g[U], dy[U];
 };
 
+// Packed dx and dg of one wave step whose stores are held back (the last
+// step of a chunk: see bwd_kernel), with the step's first row and count of
+// valid rows.
+template <int U>
+struct BwdOut {
+  u32x4 dx[U], dg[U];
+  int64_t row0;
+  int nvalid;
+};
+
 struct BwdPitch {
   uint32_t x, g, dy, dx, dg;  // row pitches in 16-byte units
 };
@@ -256,13 +271,14 @@ __device__ __forceinline__ void bwd_load(BwdRaw<U>& r,
   }
 }
 
-template <Dt T, int D, int U, bool kFull>
+template <Dt T, int D, int U, bool kFull, bool kDefer>
 __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
                                             u32x4* __restrict__ dxb,
                                             u32x4* __restrict__ dgb, BwdPitch pt,
                                             const float (&wf)[Shape<T, D>::kVec],
                                             float eps, int lane, int nvalid,
-                                            float (&acc)[Shape<T, D>::kVec]) {
+                                            float (&acc)[Shape<T, D>::kVec],
+                                            BwdOut<U>& held) {
   using S = Shape<T, D>;
   using C = typename S::C;
   constexpr int kVec = S::kVec;
@@ -302,10 +318,33 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
       q[e] *= n;  // dw contribution dy n s
     }
     if (kFull || S::kRows * u + sub < nvalid) {
-      st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), C::pack(dxf));
-      st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), C::pack(dgf));
+      if constexpr (kDefer) {
+        held.dx[u] = C::pack(dxf);
+        held.dg[u] = C::pack(dgf);
+      } else {
+        st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), C::pack(dxf));
+        st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), C::pack(dgf));
+      }
 #pragma unroll
       for (int e = 0; e < kVec; ++e) acc[e] += q[e];
+    }
+  }
+}
+
+// The stores bwd_compute held back.
+template <class S, int U>
+__device__ __forceinline__ void bwd_store_held(const BwdOut<U>& held,
+                                               u32x4* __restrict__ dx,
+                                               u32x4* __restrict__ dg, BwdPitch pt,
+                                               int lane) {
+  const int sub = lane / S::kLanes;
+  u32x4* dxb = dx + held.row0 * pt.dx;
+  u32x4* dgb = dg + held.row0 * pt.dg;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (S::kRows * u + sub < held.nvalid) {
+      st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), held.dx[u]);
+      st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), held.dg[u]);
     }
   }
 }
@@ -314,7 +353,7 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
 // rows row0(it) = chunk0 + (it*kWaves + wave)*kRows*U.  The loads of the
 // next kPrefetch steps are issued before the arithmetic of step it, so
 // every wave keeps reads in flight while it computes.
-template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kFull>
+template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kHold, bool kFull>
 __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
                                           const u32x4* __restrict__ g,
                                           const u32x4* __restrict__ dy,
@@ -323,7 +362,8 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
                                           const float (&wf)[Shape<T, D>::kVec],
                                           float eps, int64_t chunk0, int64_t rows,
                                           int wave, int lane,
-                                          float (&acc)[Shape<T, D>::kVec]) {
+                                          float (&acc)[Shape<T, D>::kVec],
+                                          BwdOut<U>& held) {
   using S = Shape<T, D>;
   constexpr int kStepRows = S::kRows * U;
   constexpr int kIters = R / (kWaves * kStepRows);
@@ -352,8 +392,17 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
     const int ahead = it + kDepth - 1;
     if (ahead < kIters) load(buf[ahead % kDepth], ahead);
     const int64_t row0 = row_of(it);
-    bwd_compute<T, D, U, kFull>(buf[it % kDepth], dx + row0 * pt.dx, dg + row0 * pt.dg,
-                                pt, wf, eps, lane, nvalid_of(it), acc);
+    if (!kHold || it + 1 < kIters) {
+      bwd_compute<T, D, U, kFull, false>(buf[it % kDepth], dx + row0 * pt.dx,
+                                         dg + row0 * pt.dg, pt, wf, eps, lane,
+                                         nvalid_of(it), acc, held);
+    } else {
+      held.row0 = row0;
+      held.nvalid = nvalid_of(it);
+      bwd_compute<T, D, U, kFull, true>(buf[it % kDepth], dx + row0 * pt.dx,
+                                        dg + row0 * pt.dg, pt, wf, eps, lane,
+                                        held.nvalid, acc, held);
+    }
   }
 }
 
@@ -466,13 +515,24 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 #endif
 constexpr bool kReducers = GRN_BWD_REDUCERS != 0;
 
+// Whether the large-tensor backward holds back its last step's stores.
+// Measured 1 % faster from 32768x48 up (BF16, D = 128) and slower below,
+// hence large tensors only.  The held registers cost occupancy where the
+// kernel is already near 256 VGPRs: FP16 at every width and BF16 at D = 256
+// would drop to one wave per SIMD, so they do not hold.  Where it holds,
+// only the timing of the stores changes: every output bit is the same.
+template <Dt T, int D>
+constexpr bool hold_large() {
+  return GRN_BWD_HOLD_LARGE != 0 && (T == Dt::f32 || (T == Dt::bf16 && D <= 128));
+}
+
 #if GRN_BWD_MIN_WAVES > 0
 #define GRN_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(GRN_BWD_MIN_WAVES)))
 #else
 #define GRN_BWD_OCCUPANCY
 #endif
 
-template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kDet>
+template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kDet, bool kHold>
 __global__ void __launch_bounds__(kWaves * kWave) GRN_BWD_OCCUPANCY
 bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, const u32x4* __restrict__ dy,
@@ -505,17 +565,19 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   // Level 1 for chunk c: dx and dg of its rows, and the column sums of its
   // dw terms (each lane's rows in step order, then the kContrib lane/wave
   // accumulators of a column in index order); valid in threads 0..D-1.
-  auto chunk_partial = [&](int64_t c) {
+  auto chunk_partial = [&](int64_t c, BwdOut<U>& held) {
     float acc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
     const int64_t chunk0 = c * R;
     if (chunk0 + R <= rows) {
-      bwd_chunk<T, D, U, kWaves, R, kPrefetch, true>(x, g, dy, dx, dg, pt, wf, eps,
-                                                     chunk0, rows, wave, lane, acc);
+      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, true>(x, g, dy, dx, dg, pt, wf, eps,
+                                                            chunk0, rows, wave, lane, acc,
+                                                            held);
     } else {
-      bwd_chunk<T, D, U, kWaves, R, kPrefetch, false>(x, g, dy, dx, dg, pt, wf, eps,
-                                                      chunk0, rows, wave, lane, acc);
+      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, false>(x, g, dy, dx, dg, pt, wf, eps,
+                                                             chunk0, rows, wave, lane, acc,
+                                                             held);
     }
     const int contrib = wave * S::kRows + sub;
 #pragma unroll
@@ -539,7 +601,12 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     int64_t grp = item - nchunks;  // for a reducer item
     if (item < nchunks) {
       const int64_t c = item;
-      const float v = chunk_partial(c);
+      // With kHold, the dx and dg stores of the chunk's last step are held
+      // back until this wave's wait for its partial's store (below) is over:
+      // that wait covers every store the wave has issued, and the freshest
+      // ones would take longest.
+      BwdOut<U> held;
+      const float v = chunk_partial(c, held);
       if constexpr (!kDet) {
         // Non-deterministic dw: the chunk sum is added with FP64 atomics
         // into one of kSlotsNd accumulators (chunk c uses slot c mod slots,
@@ -555,6 +622,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
                                  __HIP_MEMORY_SCOPE_AGENT);
           wait_memory();
         }
+        if constexpr (kHold) bwd_store_held<S, U>(held, dx, dg, pt, lane);
         __syncthreads();
         if (t == 0)
           last_overall = __hip_atomic_fetch_add(&counters[kOverallCounter], 1u, __ATOMIC_RELAXED,
@@ -588,6 +656,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
         store_coherent(partial + c * D + t, v);
         wait_memory();  // the partial is complete before anyone arrives
       }
+      if constexpr (kHold) bwd_store_held<S, U>(held, dx, dg, pt, lane);
       __syncthreads();
       grp = c / group_size;
     }
@@ -785,13 +854,14 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
     // Shapes measured fastest per size (7684x48 and 16384x32 are "mid",
     // 1031x48 "small", 32768x48 and up "large").
     if (!deterministic) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false>);
     } else if (tensor_bytes < GRN_BWD_SMALL_BYTES) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false>);
     } else if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true, false>);
     } else {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true,
+                        hold_large<T, DD>()>);
     }
     return hipGetLastError();
   });
