@@ -132,6 +132,38 @@ def test_16384x32_full_size():
     _check_dw(dw, dw_ref, torch.bfloat16, True)
 
 
+# Tensors of 256 MiB and more take the large-tensor backward; FP32 holds
+# back its last step's stores there, FP16 and BF16 at D = 256 do not.  Row
+# counts leave a ragged last chunk.
+@pytest.mark.parametrize("dname,D,rows", [("f32", 256, 270001), ("f16", 128, 1050001),
+                                          ("bf16", 256, 530001)])
+def test_large_tensor_types(dname, D, rows):
+    """Sampled rows of y, dx, dg and the whole dw (both dw types) against
+    the oracle for the large-tensor kernels of other types and widths."""
+    dtype = DTYPES[dname]
+    say(f"[dtypes] large {dname} D={D} rows={rows}")
+    inp = make_inputs(rows, D, seed=11, device="cuda", dtype=dtype)
+    y = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
+    outs = {}
+    for dw_fp32 in (False, True):
+        outs[dw_fp32] = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"],
+                                                  1e-6, dw_fp32=dw_fp32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    idx = np.unique(np.concatenate([np.arange(200), np.arange(rows - 300, rows),
+                                    rng.integers(0, rows, 1500)]))
+    ti = torch.from_numpy(idx).cuda()
+    sub = {k: (v[ti] if k != "w" else v) for k, v in inp.items()}
+    y_ref, dx_ref, dg_ref, _ = _oracle(sub, 1e-6)
+    for dw_fp32, (dx, dg, _) in outs.items():
+        _check_acts(dtype, (y[ti], dx[ti], dg[ti]), (y_ref, dx_ref, dg_ref))
+    a = {k: np.ascontiguousarray(_f64(v)) for k, v in inp.items()}
+    _, _, dw_ref = oracle.bwd(a["x"], a["g"], a["w"], a["dy"], 1e-6)
+    del a
+    for dw_fp32, (_, _, dw) in outs.items():
+        _check_dw(dw, dw_ref, dtype, dw_fp32)
+
+
 def test_f16_outputs_beyond_range_are_infinite():
     """FP16 storage: a y whose exact value lies beyond FP16's range (>= 65520
     after rounding) comes out infinite with the right sign, the rest of the
