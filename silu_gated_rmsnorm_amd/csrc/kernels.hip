@@ -598,6 +598,11 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   // streaming is done instead of amid it.
   const int64_t nwork = nchunks + (kDet && kReducers ? ngroups : 0);
   for (int64_t item = blockIdx.x; item < nwork; item += gridDim.x) {
+    // Without this compiler-only fence the non-deterministic kernel keeps
+    // values live across work items and needs 224-256 VGPRs (one wave per
+    // SIMD at D = 256 and for FP32 at D = 128); with it, 184-205.  The
+    // deterministic kernel's registers are the same either way.
+    if constexpr (!kDet) asm volatile("" ::: "memory");
     int64_t grp = item - nchunks;  // for a reducer item
     if (item < nchunks) {
       const int64_t c = item;
