@@ -56,8 +56,8 @@ R200_7684x48_US = {
 COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
-# steps, deterministic, last step's stores held back).
-BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}>"
+# steps, deterministic, last step's stores held back, fence per work item).
+BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}, false>"
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 

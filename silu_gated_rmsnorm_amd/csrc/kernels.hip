@@ -532,7 +532,8 @@ constexpr bool hold_large() {
 #define GRN_BWD_OCCUPANCY
 #endif
 
-template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kDet, bool kHold>
+template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kDet, bool kHold,
+          bool kItemFence>
 __global__ void __launch_bounds__(kWaves * kWave) GRN_BWD_OCCUPANCY
 bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, const u32x4* __restrict__ dy,
@@ -598,11 +599,13 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   // streaming is done instead of amid it.
   const int64_t nwork = nchunks + (kDet && kReducers ? ngroups : 0);
   for (int64_t item = blockIdx.x; item < nwork; item += gridDim.x) {
-    // Without this compiler-only fence the non-deterministic kernel keeps
-    // values live across work items and needs 224-256 VGPRs (one wave per
-    // SIMD at D = 256 and for FP32 at D = 128); with it, 184-205.  The
-    // deterministic kernel's registers are the same either way.
-    if constexpr (!kDet) asm volatile("" ::: "memory");
+    // A compiler-only fence at the top of each work item (kItemFence): the
+    // non-deterministic kernel then needs 184-205 VGPRs instead of 224-256
+    // (two waves per SIMD instead of one at D = 256 and for FP32 at D =
+    // 128), and runs faster below 256 MiB tensors but 1.5-3.5 % slower above
+    // (measured), where it goes without.  The deterministic kernel is
+    // unchanged by it.
+    if constexpr (kItemFence) asm volatile("" ::: "memory");
     int64_t grp = item - nchunks;  // for a reducer item
     if (item < nchunks) {
       const int64_t c = item;
@@ -857,16 +860,25 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                          L.nchunks, L.group_size, L.ngroups, L.counter_stride);
     };
     // Shapes measured fastest per size (7684x48 and 16384x32 are "mid",
-    // 1031x48 "small", 32768x48 and up "large").
+    // 1031x48 "small", 32768x48 and up "large"); the non-deterministic
+    // kernel has one shape, with the item fence below the large tier.
     if (!deterministic) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false>);
+      if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
+        launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
+                          true>);
+      } else {
+        launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
+                          false>);
+      }
     } else if (tensor_bytes < GRN_BWD_SMALL_BYTES) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false,
+                        false>);
     } else if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true, false>);
+      launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true, false,
+                        false>);
     } else {
       launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true,
-                        hold_large<T, DD>()>);
+                        hold_large<T, DD>(), false>);
     }
     return hipGetLastError();
   });
