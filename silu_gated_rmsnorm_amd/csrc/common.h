@@ -127,20 +127,39 @@ __device__ __forceinline__ float dpp_mov(float v) {
       __builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
+// v[l] + v[l ^ 16] in every lane l, from gfx950's v_permlane16_swap_b32
+// (a VALU lane swap between neighbouring 16-lane rows; no LDS).  Called
+// with both operands equal to v, it returns the lower row's value and the
+// upper row's value of each pair in every lane of the pair, and they are
+// added in that order, so both lanes get the same bits.
+__device__ __forceinline__ float add_across16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v[l] + v[l ^ 32], from v_permlane32_swap_b32 (swaps the wave's halves).
+__device__ __forceinline__ float add_across32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the kLanes lanes of a row, the result in all of them.  Steps:
 // swap neighbours, swap pairs (quad_perm), mirror within 8 lanes, mirror
-// within 16 lanes (DPP), then swaps with the lane 16 and 32 away.  Every
-// step adds two values that the partner lane adds in the other order, and
-// FP32 addition is commutative, so all lanes of a row end with the same
-// bits.  Every lane of the wave must be active.
+// within 16 lanes (DPP), then adds across 16-lane rows and wave halves
+// (lane swaps).  Every step adds two values that the partner lane adds in
+// the other order or in the same order, and FP32 addition is commutative,
+// so all lanes of a row end with the same bits.  Every lane of the wave
+// must be active.
 template <int kLanes>
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_mov<0x141>(v);  // row_half_mirror
   if constexpr (kLanes >= 16) v += dpp_mov<0x140>(v);  // row_mirror
-  if constexpr (kLanes >= 32) v += __shfl_xor(v, 16);
-  if constexpr (kLanes >= 64) v += __shfl_xor(v, 32);
+  if constexpr (kLanes >= 32) v = add_across16(v);
+  if constexpr (kLanes >= 64) v = add_across32(v);
   return v;
 }
 
