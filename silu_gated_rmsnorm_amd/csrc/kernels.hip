@@ -498,7 +498,8 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 
 // The backward: dx and dg row by row, and dw through a fixed-order tree.
 //
-// dw tree (every level in a fixed order, so the bits depend only on rows):
+// dw tree (every level in a fixed order, so for given D, type and tier the
+// bits depend only on rows):
 //  1. chunk c (R rows, one workgroup): each lane adds its rows in
 //     step order, then the lane/wave accumulators of a column are added
 //     in index order -> partial[c];
@@ -516,8 +517,8 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 constexpr bool kReducers = GRN_BWD_REDUCERS != 0;
 
 // Whether the large-tensor backward holds back its last step's stores.
-// Measured 1 % faster from 32768x48 up (BF16, D = 128) and slower below,
-// hence large tensors only.  The held registers cost occupancy where the
+// Measured 1-2 % faster from 65536x48 up (BF16, D = 128), no change at
+// 32768x48 and slower at smaller sizes, hence large tensors only.  The held registers cost occupancy where the
 // kernel is already near 256 VGPRs: FP16 at every width and BF16 at D = 256
 // would drop to one wave per SIMD, so they do not hold.  Where it holds,
 // only the timing of the stores changes: every output bit is the same.
