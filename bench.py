@@ -270,7 +270,7 @@ def main():
         bwd_us = rotate_time(op_bwd, R)
         rec("bwd", bwd_us, bwd_bytes)
         rec("bwd_f32", rotate_time(lambda st: op_bwd(st, True), R), bwd32_bytes)
-        # A/B: dw summed with float atomics instead of the fixed-order tree.
+        # A/B: dw summed with FP64 atomics instead of the fixed-order tree.
         rec("bwd_nondet", rotate_time(lambda st: op_bwd(st, False, False), R), bwd_bytes)
         rec("bwd_nondet_f32", rotate_time(lambda st: op_bwd(st, True, False), R),
             bwd32_bytes)
