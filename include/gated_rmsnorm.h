@@ -96,7 +96,7 @@ enum { GRN_DTYPE_BF16 = 0, GRN_DTYPE_F16 = 1, GRN_DTYPE_F32 = 2 };
 
 /* Bytes of device workspace the backward needs for `rows` rows of width D,
  * for any element type: a fixed region of arrival counters, one FP32
- * partial dw of D values per chunk of rows (at most 128 rows a chunk, see
+ * partial dw of D values per chunk of rows (128 or 256 rows a chunk, see
  * gated_rmsnorm_chunk_rows), and one per group of about sqrt(chunks)
  * chunks.  Returns 0 for rows <= 0 or an unsupported D.
  *
