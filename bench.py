@@ -56,7 +56,13 @@ R200_7684x48_US = {
     "det_fwd": 34.641, "det_bwdg": 65.896, "det_ckptg": 132.328,
 }
 
-COUNTERS_FILE = ROOT / "profiles" / "bwd_kernel_7684x48_traffic.json"
+PROFILES_DIR = ROOT / "profiles"
+
+
+def counters_file(workload):
+    """Committed HBM-traffic figures of the kernels for one workload."""
+    return PROFILES_DIR / f"bwd_kernel_{workload}_traffic.json"
+
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
 # steps, deterministic, last step's stores held back, fence per work item).
@@ -426,7 +432,7 @@ def traffic_from_counters(workload):
     the figure does not apply (None).
     """
     try:
-        rec = json.loads(COUNTERS_FILE.read_text())
+        rec = json.loads(counters_file(workload).read_text())
     except (OSError, ValueError):
         return None
     if rec.get("workload") != workload:
@@ -502,8 +508,9 @@ def summarize_counters(fetch_csv, write_csv, workload="7684x48"):
            "fetch_scale": round(scale_f, 6), "write_scale": round(scale_w, 6),
            "kernels": kernels,
            "hbm_bytes_per_launch": kernels.get("bwd_kernel", {}).get("hbm_bytes_per_launch")}
-    COUNTERS_FILE.parent.mkdir(exist_ok=True)
-    COUNTERS_FILE.write_text(json.dumps(rec, indent=1) + "\n")
+    out = counters_file(workload)
+    out.parent.mkdir(exist_ok=True)
+    out.write_text(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec, indent=1))
 
 

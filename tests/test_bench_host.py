@@ -37,7 +37,7 @@ def counters(tmp_path, monkeypatch):
     src = tmp_path / "kernels.hip"
     src.write_text("// kernel source v1\n")
     monkeypatch.setattr(bench, "KERNEL_SOURCE", src)
-    monkeypatch.setattr(bench, "COUNTERS_FILE", tmp_path / "traffic.json")
+    monkeypatch.setattr(bench, "PROFILES_DIR", tmp_path)
     from silu_gated_rmsnorm_amd.inputs import WORKLOADS
     rows = WORKLOADS["1031x48"].rows
     copy = rows * 256                       # bytes of one BF16 [rows, 128] tensor
@@ -54,7 +54,7 @@ def counters(tmp_path, monkeypatch):
     _write_csv(tmp_path / "w.csv", "WRITE_SIZE", write_rows)
     bench.summarize_counters(tmp_path / "f.csv", tmp_path / "w.csv", workload="1031x48")
     return {"src": src, "copy": copy, "rows": rows,
-            "rec": json.loads((tmp_path / "traffic.json").read_text())}
+            "rec": json.loads((tmp_path / "bwd_kernel_1031x48_traffic.json").read_text())}
 
 
 def test_scaling(counters):
@@ -74,6 +74,6 @@ def test_scaling(counters):
 
 def test_traffic_applies_only_to_its_workload_and_source(counters):
     assert bench.traffic_from_counters("1031x48") == 5 * counters["copy"]
-    assert bench.traffic_from_counters("7684x48") is None
+    assert bench.traffic_from_counters("7684x48") is None   # no file for it here
     counters["src"].write_text("// kernel source v2\n")
     assert bench.traffic_from_counters("1031x48") is None
