@@ -191,6 +191,32 @@ def test_full_size_sampled(name):
     say(f"  dw fp32 rel err {e32:.2e}, dw bf16 worst {u16} ulp")
 
 
+def test_tensors_beyond_4gib():
+    """17,000,000 rows: each BF16 tensor is 4.35 GB, so byte offsets pass
+    2^32 at row 16,777,216.  Rows on both sides of that boundary, sampled
+    rows elsewhere and the whole dw (FP32 and BF16) against the oracle."""
+    rows = 17_000_000
+    say(f"[parity] rows={rows}: tensors beyond 4 GiB")
+    inp = make_inputs(rows, seed=17, device="cuda")
+    y, dx, dg, dw32 = gpu_all(inp, EPS, True)
+    boundary = (1 << 32) // (128 * 2)
+    idx_np = _sample_rows(rows, np.arange(boundary - 300, boundary + 300), seed=5)
+    idx = torch.from_numpy(idx_np).cuda()
+    sub = {k: (v[idx] if k != "w" else v) for k, v in inp.items()}
+    y_ref, dx_ref, dg_ref, _ = oracle_all(sub, EPS, want_dw=False)
+    assert_acts_close("y", y[idx], y_ref)
+    assert_acts_close("dx", dx[idx], dx_ref)
+    assert_acts_close("dg", dg[idx], dg_ref)
+    del y, dx, dg
+    dw_ref = oracle_dw_streamed(inp, EPS)
+    e32 = assert_dw_close(dw32, dw_ref, True)
+    _, _, dw16 = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], EPS,
+                                           dw_fp32=False)
+    torch.cuda.synchronize()
+    u16 = assert_dw_close(dw16, dw_ref, False)
+    say(f"  dw fp32 rel err {e32:.2e}, dw bf16 worst {u16} ulp")
+
+
 # --------------------------------------------------------------------------
 # Strided rows: x and g as the two halves of a fused projection, outputs
 # into strided views.  Results must be bitwise those of packed copies.
