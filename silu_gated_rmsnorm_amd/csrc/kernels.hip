@@ -69,6 +69,11 @@
 #ifndef GRN_BWD_HOLD_LARGE
 #define GRN_BWD_HOLD_LARGE 1
 #endif
+// Steps without prefetch (the middle tier): issue the next step's loads
+// before this step's stores (see bwd_chunk).
+#ifndef GRN_BWD_LBS
+#define GRN_BWD_LBS 1
+#endif
 #ifndef GRN_BWD_U_ND
 #define GRN_BWD_U_ND 4       // the non-deterministic dw kernel, all sizes
 #endif
@@ -319,8 +324,10 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
     }
     if (kFull || S::kRows * u + sub < nvalid) {
       if constexpr (kDefer) {
-        held.dx[u] = C::pack(dxf);
-        held.dg[u] = C::pack(dgf);
+        // Packed here, not where they are stored: the opaque copies keep
+        // the compiler from carrying the FP32 values to the stores.
+        held.dx[u] = use_when_needed(C::pack(dxf));
+        held.dg[u] = use_when_needed(C::pack(dgf));
       } else {
         st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), C::pack(dxf));
         st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), C::pack(dgf));
@@ -331,8 +338,8 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
   }
 }
 
-// The stores bwd_compute held back.
-template <class S, int U>
+// The stores bwd_compute held back (kFull: every row of the step is valid).
+template <class S, int U, bool kFull = false>
 __device__ __forceinline__ void bwd_store_held(const BwdOut<U>& held,
                                                u32x4* __restrict__ dx,
                                                u32x4* __restrict__ dg, BwdPitch pt,
@@ -342,7 +349,7 @@ __device__ __forceinline__ void bwd_store_held(const BwdOut<U>& held,
   u32x4* dgb = dg + held.row0 * pt.dg;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (S::kRows * u + sub < held.nvalid) {
+    if (kFull || S::kRows * u + sub < held.nvalid) {
       st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), held.dx[u]);
       st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), held.dg[u]);
     }
@@ -353,7 +360,8 @@ __device__ __forceinline__ void bwd_store_held(const BwdOut<U>& held,
 // rows row0(it) = chunk0 + (it*kWaves + wave)*kRows*U.  The loads of the
 // next kPrefetch steps are issued before the arithmetic of step it, so
 // every wave keeps reads in flight while it computes.
-template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kHold, bool kFull>
+template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kHold, bool kLbs,
+          bool kFull>
 __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
                                           const u32x4* __restrict__ g,
                                           const u32x4* __restrict__ dy,
@@ -374,6 +382,42 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
     const int64_t left = rows - row_of(it);
     return (int)(left < 0 ? 0 : (left > kStepRows ? kStepRows : left));
   };
+  if constexpr (kLbs) {
+    // Without prefetch, the next step's loads go out after this step's
+    // arithmetic but before its stores.  A wave's memory counter retires
+    // loads and stores in issue order, so loads issued after the stores
+    // would also wait for the stores to complete; this order keeps the
+    // next loads independent of them, at the cost of this step's packed
+    // outputs waiting in registers (measured: 7684x48 fwd + bwd 121.7 ->
+    // 120.8 us, FP32 D = 128 backward 178 -> 173 us).
+    static_assert(kPrefetch == 0, "the step order without prefetch");
+    BwdRaw<U> b;
+    auto load1 = [&](int it) {
+      const int64_t row0 = row_of(it);
+      bwd_load<S, U, kFull>(b, x + row0 * pt.x, g + row0 * pt.g, dy + row0 * pt.dy, pt,
+                            lane, nvalid_of(it));
+    };
+    load1(0);
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      BwdOut<U> out;
+      out.row0 = row_of(it);
+      out.nvalid = nvalid_of(it);
+      bwd_compute<T, D, U, kFull, true>(b, dx + out.row0 * pt.dx, dg + out.row0 * pt.dg, pt,
+                                        wf, eps, lane, out.nvalid, acc, out);
+      if (it + 1 < kIters) {
+        asm volatile("" ::: "memory");  // keep the loads after this step's arithmetic
+        load1(it + 1);
+      }
+      if (kHold && it + 1 == kIters) {
+        held = out;
+      } else {
+        bwd_store_held<S, U, kFull>(out, dx, dg, pt, lane);
+        asm volatile("" ::: "memory");  // and the stores before the next step
+      }
+    }
+    return;
+  }
   // A ring of kDepth register buffers: step it+kDepth-1 is loaded while
   // step it is computed.
   constexpr int kDepth = kPrefetch + 1;
@@ -553,6 +597,9 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   constexpr int kContrib = kWaves * S::kRows;
   static_assert(kContrib * D >= 4 * kThreads, "LDS of level 1 serves the column sums");
   constexpr int kSlotsNd = nondet_slots(D);
+  // Loads before stores in the deterministic kernel without prefetch, except
+  // for FP16, whose packed outputs would push it to one wave per SIMD.
+  constexpr bool kLbs = GRN_BWD_LBS != 0 && kDet && kPrefetch == 0 && T != Dt::f16;
   __shared__ float red[kContrib][D];
   __shared__ int last_in_group, last_overall;
 
@@ -573,13 +620,13 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
     const int64_t chunk0 = c * R;
     if (chunk0 + R <= rows) {
-      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, true>(x, g, dy, dx, dg, pt, wf, eps,
-                                                            chunk0, rows, wave, lane, acc,
-                                                            held);
+      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, true>(x, g, dy, dx, dg, pt, wf,
+                                                                  eps, chunk0, rows, wave,
+                                                                  lane, acc, held);
     } else {
-      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, false>(x, g, dy, dx, dg, pt, wf, eps,
-                                                             chunk0, rows, wave, lane, acc,
-                                                             held);
+      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, false>(x, g, dy, dx, dg, pt, wf,
+                                                                   eps, chunk0, rows, wave,
+                                                                   lane, acc, held);
     }
     const int contrib = wave * S::kRows + sub;
 #pragma unroll
