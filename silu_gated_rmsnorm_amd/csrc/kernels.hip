@@ -388,8 +388,7 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
     // loads and stores in issue order, so loads issued after the stores
     // would also wait for the stores to complete; this order keeps the
     // next loads independent of them, at the cost of this step's packed
-    // outputs waiting in registers (measured: 7684x48 fwd + bwd 121.7 ->
-    // 120.8 us, FP32 D = 128 backward 178 -> 173 us).
+    // outputs waiting in registers (lbs_mid() says where it pays).
     static_assert(kPrefetch == 0, "the step order without prefetch");
     BwdRaw<U> b;
     auto load1 = [&](int it) {
@@ -560,6 +559,18 @@ __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v
 #endif
 constexpr bool kReducers = GRN_BWD_REDUCERS != 0;
 
+// Whether the deterministic middle-tier backward (no prefetch) issues the
+// next step's loads before this step's stores (bwd_chunk).  Measured on the
+// backward alone at 7684x48 rows: FP32 D = 64 / 128 / 256 84.3 -> 82.8,
+// 178 -> 173, 362 -> 359 us and BF16 D = 256 179 -> 175 us, but BF16 D = 128
+// 82.6 -> 83.1 us and D = 64 45.8 -> 46.2 us (fwd + bwd back to back gains
+// there, from the rows the forward leaves in the caches); FP16 would drop to
+// one wave per SIMD.  Only the timing of the accesses changes.
+template <Dt T, int D>
+constexpr bool lbs_mid() {
+  return GRN_BWD_LBS != 0 && (T == Dt::f32 || (T == Dt::bf16 && D == 256));
+}
+
 // Whether the large-tensor backward holds back its last step's stores.
 // Measured 1-2 % faster from 65536x48 up (BF16, D = 128), no change at
 // 32768x48 and slower at smaller sizes, hence large tensors only.  The held registers cost occupancy where the
@@ -597,9 +608,7 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   constexpr int kContrib = kWaves * S::kRows;
   static_assert(kContrib * D >= 4 * kThreads, "LDS of level 1 serves the column sums");
   constexpr int kSlotsNd = nondet_slots(D);
-  // Loads before stores in the deterministic kernel without prefetch, except
-  // for FP16, whose packed outputs would push it to one wave per SIMD.
-  constexpr bool kLbs = GRN_BWD_LBS != 0 && kDet && kPrefetch == 0 && T != Dt::f16;
+  constexpr bool kLbs = kDet && kPrefetch == 0 && lbs_mid<T, D>();
   __shared__ float red[kContrib][D];
   __shared__ int last_in_group, last_overall;
 
