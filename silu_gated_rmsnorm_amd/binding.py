@@ -130,6 +130,8 @@ def _act(name: str, t: torch.Tensor, like=None):
         raise ValueError(f"{name}: expected shape [rows, D], D in {SUPPORTED_D}, "
                          f"got {tuple(t.shape)}")
     if like is not None:
+        if t.device != like.device:
+            raise ValueError(f"{name}: expected a tensor on {like.device}, got {t.device}")
         if t.dtype != like.dtype:
             raise TypeError(f"{name}: expected {like.dtype}, got {t.dtype}")
         if tuple(t.shape) != tuple(like.shape):
@@ -145,6 +147,8 @@ def _weight(w: torch.Tensor, x: torch.Tensor) -> int:
     if not isinstance(w, torch.Tensor) or w.device.type != "cuda":
         raise TypeError("w: expected a GPU tensor")
     D = x.shape[1]
+    if w.device != x.device:
+        raise ValueError(f"w: expected a tensor on {x.device}, got {w.device}")
     if w.dtype != x.dtype or w.shape != (D,) or not w.is_contiguous():
         raise ValueError(f"w: expected a contiguous {x.dtype} [{D}] tensor")
     return w.data_ptr()
