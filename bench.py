@@ -80,6 +80,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="7684x48")
+    p.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3,
+                   help="untimed steps over every buffer set before the warm-up, in ms")
     p.add_argument("--dtype", choices=("bf16", "f16", "f32"), default="bf16",
                    help="storage type of x, g, dy, w and the outputs (the pages: bf16)")
     p.add_argument("--dim", type=int, choices=(64, 128, 256), default=D,
@@ -246,7 +248,7 @@ def main():
             for st in sets:
                 fn(st)
             torch.cuda.synchronize()
-            if time.perf_counter() - t0 >= SETTLE_S:
+            if time.perf_counter() - t0 >= args.settle_ms * 1e-3:
                 break
 
     if args.profile_op:
