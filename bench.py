@@ -65,8 +65,10 @@ def counters_file(workload):
 
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
-# steps, deterministic, last step's stores held back, fence per work item).
-BWD_KERNEL = "grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}, false>"
+# steps, deterministic, last step's stores held back, fence per work item,
+# window of chunks whose blocks interleave: 256 below 256 MiB tensors, else 0).
+BWD_KERNEL = ("grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}, false, "
+              "{SWZ}>")
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 
@@ -384,7 +386,8 @@ def main():
         u, pf = (2, 1) if tb < (32 << 20) else ((4, 0) if tb < (256 << 20) else (4, 1))
         hold = tb >= (256 << 20) and (args.dtype == "f32" or (args.dtype == "bf16" and D <= 128))
         kname = BWD_KERNEL.format(code=dt_code, D=D, U=u, R=256 if row_bytes <= 128 else 128,
-                                  PF=pf, HOLD="true" if hold else "false")
+                                  PF=pf, HOLD="true" if hold else "false",
+                                  SWZ=256 if tb < (256 << 20) else 0)
         roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -228,9 +228,10 @@ fwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
 // the row size: chunk_rows_for()).
 //
 // The dw order is fixed by the chunk alone: within chunk c, wave v of the
-// workgroup takes step `it` on rows c*R + (it*kWaves + v)*kRows*U + kRows*u
-// + l/kLanes, and lane l adds its kVec columns' contributions in (it, u)
-// order into FP32 registers.  At the end of the chunk the kWaves*kRows
+// workgroup takes step `it` on rows row0(c) + it*stride(c) + v*kRows*U +
+// kRows*u + l/kLanes (chunk_blocks(): contiguous chunks have row0 = c*R and
+// stride = kWaves*kRows*U), and lane l adds its kVec columns' contributions
+// in (it, u) order into FP32 registers.  At the end of the chunk the kWaves*kRows
 // (wave, row-in-group) accumulators of each column are added in index order
 // through LDS.  Which workgroup runs a chunk, and when, changes nothing, so
 // dw does not depend on the grid or on timing.
@@ -357,7 +358,8 @@ __device__ __forceinline__ void bwd_store_held(const BwdOut<U>& held,
 }
 
 // One chunk for one workgroup: wave `wave` takes steps it = 0..kIters-1 on
-// rows row0(it) = chunk0 + (it*kWaves + wave)*kRows*U.  The loads of the
+// rows row0(it) = chunk0 + it*it_stride + wave*kRows*U (it_stride is
+// kWaves*kRows*U for a contiguous chunk: chunk_blocks()).  The loads of the
 // next kPrefetch steps are issued before the arithmetic of step it, so
 // every wave keeps reads in flight while it computes.
 template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kHold, bool kLbs,
@@ -368,7 +370,8 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
                                           u32x4* __restrict__ dx,
                                           u32x4* __restrict__ dg, BwdPitch pt,
                                           const float (&wf)[Shape<T, D>::kVec],
-                                          float eps, int64_t chunk0, int64_t rows,
+                                          float eps, int64_t chunk0, int64_t it_stride,
+                                          int64_t rows,
                                           int wave, int lane,
                                           float (&acc)[Shape<T, D>::kVec],
                                           BwdOut<U>& held) {
@@ -376,7 +379,7 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
   constexpr int kStepRows = S::kRows * U;
   constexpr int kIters = R / (kWaves * kStepRows);
   auto row_of = [&](int it) {
-    return chunk0 + (int64_t)(it * kWaves + wave) * kStepRows;
+    return chunk0 + it * it_stride + (int64_t)wave * kStepRows;
   };
   auto nvalid_of = [&](int it) {
     const int64_t left = rows - row_of(it);
@@ -529,6 +532,55 @@ __device__ __forceinline__ float column_sum_fixed(const float* __restrict__ src,
   return res;
 }
 
+// Which rows make up chunk c.  A chunk is R/B blocks of B rows (B: the rows
+// a workgroup step covers), block it starting at row0 + it*stride.
+//  * W = 0: the chunk is rows [c*R, c*R + R) (stride B).
+//  * W > 0: chunks are taken in windows of W; within the
+//    window of chunks [s*W, s*W + Ws), block it of its j-th chunk is block
+//    s*W*(R/B) + it*Ws + j of the tensor.  The windows tile the rows in
+//    order, so the mapping is a bijection onto blocks (the last window has
+//    Ws = nchunks - s*W <= W chunks); blocks at or past the end of the rows
+//    are empty.  Chunks resident at the same time then read neighbouring
+//    blocks at each step, instead of one block of each of W separate chunks.
+// `end` is one past the chunk's last row (for its last, highest block).
+// The mapping depends on c, nchunks and the shape only, never on the grid.
+//
+// Measured (backward alone, BF16 D = 128, same process, alternating): with
+// W = 256 chunks (a chunk's two blocks 4 MiB apart per tensor) 1031x48
+// 17.48 -> 17.18 us, 3534x48 44.3 -> 43.4, 7684x48 82.8 -> 81.9, 12296x48
+// 128.3 -> 127.0, 16384x32 115.2 -> 113.4; W = 64 and 128 were slower than
+// contiguous chunks at most of these sizes, and every W tried (256, 512,
+// 1024) was 1-2 % slower from 32768x48 up, where both of a wave's steps are
+// loaded at once and contiguous chunks stay (launch_bwd).
+#ifndef GRN_BWD_SWZ_MID
+#define GRN_BWD_SWZ_MID 256   // window below GRN_BWD_LARGE_BYTES
+#endif
+#ifndef GRN_BWD_SWZ_LARGE
+#define GRN_BWD_SWZ_LARGE 0   // window from GRN_BWD_LARGE_BYTES up
+#endif
+struct ChunkBlocks {
+  int64_t row0, stride, end;
+};
+
+template <int R, int B, int kW>
+__device__ __forceinline__ ChunkBlocks chunk_blocks(int64_t c, int64_t nchunks) {
+  constexpr int kBlocks = R / B;
+  ChunkBlocks cb;
+  if constexpr (kW == 0) {
+    cb.row0 = c * R;
+    cb.stride = B;
+  } else {
+    constexpr int64_t W = kW;
+    const int64_t s = c / W;
+    const int64_t j = c - s * W;
+    const int64_t ws = (nchunks - s * W) < W ? (nchunks - s * W) : W;
+    cb.row0 = (s * W * kBlocks + j) * B;
+    cb.stride = ws * B;
+  }
+  cb.end = cb.row0 + (kBlocks - 1) * cb.stride + B;
+  return cb;
+}
+
 // dw[col] = v in FP32, or rounded once to the input type.
 template <Dt T>
 __device__ __forceinline__ void store_dw(void* dw, int dw_fp32, int col, float v) {
@@ -589,7 +641,7 @@ constexpr bool hold_large() {
 #endif
 
 template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kDet, bool kHold,
-          bool kItemFence>
+          bool kItemFence, int kSwz>
 __global__ void __launch_bounds__(kWaves * kWave) GRN_BWD_OCCUPANCY
 bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, const u32x4* __restrict__ dy,
@@ -627,15 +679,13 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     float acc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
-    const int64_t chunk0 = c * R;
-    if (chunk0 + R <= rows) {
-      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, true>(x, g, dy, dx, dg, pt, wf,
-                                                                  eps, chunk0, rows, wave,
-                                                                  lane, acc, held);
+    const ChunkBlocks cb = chunk_blocks<R, kWaves * kStepRows, kSwz>(c, nchunks);
+    if (cb.end <= rows) {
+      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, true>(
+          x, g, dy, dx, dg, pt, wf, eps, cb.row0, cb.stride, rows, wave, lane, acc, held);
     } else {
-      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, false>(x, g, dy, dx, dg, pt, wf,
-                                                                   eps, chunk0, rows, wave,
-                                                                   lane, acc, held);
+      bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, false>(
+          x, g, dy, dx, dg, pt, wf, eps, cb.row0, cb.stride, rows, wave, lane, acc, held);
     }
     const int contrib = wave * S::kRows + sub;
 #pragma unroll
@@ -922,20 +972,20 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
     if (!deterministic) {
       if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
         launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
-                          true>);
+                          true, GRN_BWD_SWZ_MID>);
       } else {
         launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
-                          false>);
+                          false, GRN_BWD_SWZ_LARGE>);
       }
     } else if (tensor_bytes < GRN_BWD_SMALL_BYTES) {
       launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false,
-                        false>);
+                        false, GRN_BWD_SWZ_MID>);
     } else if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
       launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true, false,
-                        false>);
+                        false, GRN_BWD_SWZ_MID>);
     } else {
       launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true,
-                        hold_large<T, DD>(), false>);
+                        hold_large<T, DD>(), false, GRN_BWD_SWZ_LARGE>);
     }
     return hipGetLastError();
   });
