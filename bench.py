@@ -66,7 +66,7 @@ def counters_file(workload):
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
 # steps, deterministic, last step's stores held back, fence per work item,
-# window of chunks whose blocks interleave: 256 below 256 MiB tensors, else 0).
+# window of chunks whose blocks interleave: 0 for the prefetching shape).
 BWD_KERNEL = ("grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}, false, "
               "{SWZ}>")
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
@@ -380,14 +380,17 @@ def main():
         per_launch = bwd_bytes
         achieved = per_launch / (bwd_us * 1e-6) / 1e9
         # The library picks the backward's shape by tensor size (32 MiB and
-        # 256 MiB boundaries): row groups per wave step, prefetched steps and
-        # (large tensors of FP32, or BF16 up to D = 128) held stores.
+        # 256 MiB boundaries), and above 256 MiB by type and width: row
+        # groups per wave step, prefetched steps, held stores and the window
+        # of interleaved chunks.
         tb = rows * row_bytes
-        u, pf = (2, 1) if tb < (32 << 20) else ((4, 0) if tb < (256 << 20) else (4, 1))
-        hold = tb >= (256 << 20) and (args.dtype == "f32" or (args.dtype == "bf16" and D <= 128))
+        prefetch = tb >= (256 << 20) and ((args.dtype == "f16" and D <= 128) or
+                                          (args.dtype == "bf16" and D == 64))
+        u, pf = (2, 1) if tb < (32 << 20) else ((4, 1) if prefetch else (4, 0))
+        hold = prefetch and args.dtype == "bf16"
         kname = BWD_KERNEL.format(code=dt_code, D=D, U=u, R=256 if row_bytes <= 128 else 128,
                                   PF=pf, HOLD="true" if hold else "false",
-                                  SWZ=256 if tb < (256 << 20) else 0)
+                                  SWZ=0 if prefetch else 256)
         roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),

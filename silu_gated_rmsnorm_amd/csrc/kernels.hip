@@ -38,8 +38,10 @@
 #endif
 // Backward shape by tensor size (bytes of one [rows, D] activation):
 // row groups per wave step (U) and steps of loads prefetched ahead (PF).
-// U changes the order in which a chunk's rows are added into dw, so dw's
-// bits depend on the tier, which depends only on rows, D and the type.
+// From GRN_BWD_LARGE_BYTES up only some types and widths take the LARGE
+// shape (prefetch_large()); the others keep the MID one.  U and the chunk
+// layout change the order in which a chunk's rows are added into dw, so
+// dw's bits depend on the tier, which depends only on rows, D and the type.
 #ifndef GRN_BWD_SMALL_BYTES
 #define GRN_BWD_SMALL_BYTES (32ll << 20)
 #endif
@@ -549,14 +551,11 @@ __device__ __forceinline__ float column_sum_fixed(const float* __restrict__ src,
 // W = 256 chunks (a chunk's two blocks 4 MiB apart per tensor) 1031x48
 // 17.48 -> 17.18 us, 3534x48 44.3 -> 43.4, 7684x48 82.8 -> 81.9, 12296x48
 // 128.3 -> 127.0, 16384x32 115.2 -> 113.4; W = 64 and 128 were slower than
-// contiguous chunks at most of these sizes, and every W tried (256, 512,
-// 1024) was 1-2 % slower from 32768x48 up, where both of a wave's steps are
-// loaded at once and contiguous chunks stay (launch_bwd).
-#ifndef GRN_BWD_SWZ_MID
-#define GRN_BWD_SWZ_MID 256   // window below GRN_BWD_LARGE_BYTES
-#endif
-#ifndef GRN_BWD_SWZ_LARGE
-#define GRN_BWD_SWZ_LARGE 0   // window from GRN_BWD_LARGE_BYTES up
+// contiguous chunks at most of these sizes.  The shape that loads both of a
+// wave's steps at once (prefetch_large()) was 1-2 % slower with every W
+// tried (256, 512, 1024) and keeps contiguous chunks.
+#ifndef GRN_BWD_SWZ
+#define GRN_BWD_SWZ 256   // window of the shapes without prefetch
 #endif
 struct ChunkBlocks {
   int64_t row0, stride, end;
@@ -623,15 +622,33 @@ constexpr bool lbs_mid() {
   return GRN_BWD_LBS != 0 && (T == Dt::f32 || (T == Dt::bf16 && D == 256));
 }
 
-// Whether the large-tensor backward holds back its last step's stores.
-// Measured 1-2 % faster from 65536x48 up (BF16, D = 128), no change at
-// 32768x48 and slower at smaller sizes, hence large tensors only.  The held registers cost occupancy where the
-// kernel is already near 256 VGPRs: FP16 at every width and BF16 at D = 256
-// would drop to one wave per SIMD, so they do not hold.  Where it holds,
-// only the timing of the stores changes: every output bit is the same.
+// Whether the large-tensor (prefetching) backward holds back its last
+// step's stores.  Measured 1-2 % faster from 65536x48 up with BF16 at
+// D = 128 (which has since moved to the middle shape), no change at 32768x48
+// and slower at smaller sizes, hence large tensors only; of the types and
+// widths that take the prefetching shape, BF16 at D = 64 holds.  The held
+// registers cost occupancy where the kernel is already near 256 VGPRs: FP16
+// at every width would drop to one wave per SIMD, so it does not hold.
+// Where it holds, only the timing of the stores changes: every output bit
+// is the same.
 template <Dt T, int D>
 constexpr bool hold_large() {
   return GRN_BWD_HOLD_LARGE != 0 && (T == Dt::f32 || (T == Dt::bf16 && D <= 128));
+}
+
+// Whether tensors of GRN_BWD_LARGE_BYTES and more take the shape that loads
+// both of a wave's steps at once (otherwise the middle tier's shape, with
+// interleaved chunk blocks, serves them too).  Measured per type and width
+// (backward alone, same process, alternating; us, prefetching shape vs
+// middle shape): FP16 D = 128 at 32768x48 / 65536x48 327 vs 329 / 658 vs
+// 683, FP16 D = 64 at 65536x48 325 vs 330, BF16 D = 64 at 65536x48 332 vs
+// 334; but BF16 D = 128 at 32768x48 / 65536x48 / 262144x48 335 vs 329 /
+// 665 vs 665 / 2,823 vs 2,756, BF16 D = 256 at 32768x48 737 vs 684, FP16
+// D = 256 748 vs 680, FP32 D = 64 / 128 at 32768x48 342 vs 338 / 751 vs
+// 689, FP32 D = 256 at 7684x48 rows 362 vs 337.
+template <Dt T, int D>
+constexpr bool prefetch_large() {
+  return (T == Dt::f16 && D <= 128) || (T == Dt::bf16 && D == 64);
 }
 
 #if GRN_BWD_MIN_WAVES > 0
@@ -966,26 +983,27 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                          reinterpret_cast<uint32_t*>(ws), dw, dw_fp32, rows, eps,
                          L.nchunks, L.group_size, L.ngroups, L.counter_stride);
     };
-    // Shapes measured fastest per size (7684x48 and 16384x32 are "mid",
-    // 1031x48 "small", 32768x48 and up "large"); the non-deterministic
-    // kernel has one shape, with the item fence below the large tier.
+    // Shapes measured fastest per size (1031x48 is "small", 7684x48 and up
+    // "mid"; tensors of 256 MiB and more take the prefetching shape only
+    // where prefetch_large() says so); the non-deterministic kernel has one
+    // shape, with the item fence below 256 MiB tensors.
     if (!deterministic) {
       if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
         launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
-                          true, GRN_BWD_SWZ_MID>);
+                          true, GRN_BWD_SWZ>);
       } else {
         launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
-                          false, GRN_BWD_SWZ_LARGE>);
+                          false, GRN_BWD_SWZ>);
       }
     } else if (tensor_bytes < GRN_BWD_SMALL_BYTES) {
       launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false,
-                        false, GRN_BWD_SWZ_MID>);
-    } else if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
+                        false, GRN_BWD_SWZ>);
+    } else if (tensor_bytes < GRN_BWD_LARGE_BYTES || !prefetch_large<T, DD>()) {
       launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true, false,
-                        false, GRN_BWD_SWZ_MID>);
+                        false, GRN_BWD_SWZ>);
     } else {
       launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true,
-                        hold_large<T, DD>(), false, GRN_BWD_SWZ_LARGE>);
+                        hold_large<T, DD>(), false, 0>);
     }
     return hipGetLastError();
   });
