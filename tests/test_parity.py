@@ -126,6 +126,32 @@ def test_every_output_element_written():
         assert not torch.isnan(t).any().item()
 
 
+@pytest.mark.parametrize("rows", [70363, 173741])
+def test_interleaved_chunks_every_row(rows):
+    """The backward takes a chunk's row blocks from windows of 256 chunks.
+
+    70,363 rows (17 MiB per tensor, the small-tensor shape) have 550 chunks:
+    two full windows and a last one of 38 chunks whose last chunk holds 91
+    rows; 173,741 rows (42 MiB, the middle shape) have 1,358 chunks, a last
+    window of 78 and a last chunk of 45 rows.  dx and dg start as NaN: every
+    row must be written, and every element must match the oracle, as must
+    dw (both types) and dx/dg of the non-deterministic kernel."""
+    say(f"[parity] interleaved chunk layout rows={rows}")
+    inp = make_inputs(rows, seed=rows % 1000, device="cuda")
+    _, dx_ref, dg_ref, dw_ref = oracle_all(inp, EPS)
+    for dw_fp32, det in ((True, True), (False, True), (True, False)):
+        nan = lambda: torch.full((rows, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dx, dg = nan(), nan()
+        _, _, dw = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], EPS,
+                                             dw_fp32=dw_fp32, dx=dx, dg=dg,
+                                             deterministic=det)
+        torch.cuda.synchronize()
+        assert not torch.isnan(dx).any().item() and not torch.isnan(dg).any().item()
+        assert_acts_close("dx", dx, dx_ref)
+        assert_acts_close("dg", dg, dg_ref)
+        assert_dw_close(dw, dw_ref, dw_fp32)
+
+
 def test_adjacent_buffers_accepted():
     """Inputs and outputs packed back to back in one allocation (no overlap)."""
     rows = 300
