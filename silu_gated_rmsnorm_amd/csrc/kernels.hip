@@ -716,12 +716,17 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     return v;
   };
 
-  // Work items: chunks [0, nchunks), then (deterministic dw) one reducer
-  // item per group, which arrives at its group's counter like a chunk but
-  // carries no partial.  Being last in the grid, reducers usually arrive
-  // after all of their group's chunks, so most group sums run once the
-  // streaming is done instead of amid it.
-  const int64_t nwork = nchunks + (kDet && kReducers ? ngroups : 0);
+  // Work items: chunks [0, nchunks - K), then 2K claim items that take the
+  // last K chunks at run time (claim_chunks(); K = 0 for the
+  // non-deterministic dw and for small grids), then (deterministic dw) one
+  // reducer item per group, which arrives at its group's counter like a
+  // chunk but carries no partial.  Being last in the grid, reducers usually
+  // arrive after all of their group's chunks, so most group sums run once
+  // the streaming is done instead of amid it.
+  const int64_t K = claim_chunks(kDet, nchunks);
+  const int64_t nstatic = nchunks - K;
+  const int64_t nwork = nchunks + K + (kDet && kReducers ? ngroups : 0);
+  __shared__ uint32_t claimed;
   for (int64_t item = blockIdx.x; item < nwork; item += gridDim.x) {
     // A compiler-only fence at the top of each work item (kItemFence): the
     // non-deterministic kernel then needs 184-205 VGPRs instead of 224-256
@@ -730,9 +735,30 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     // (measured), where it goes without.  The deterministic kernel is
     // unchanged by it.
     if constexpr (kItemFence) asm volatile("" ::: "memory");
-    int64_t grp = item - nchunks;  // for a reducer item
-    if (item < nchunks) {
-      const int64_t c = item;
+    int64_t grp = item - nchunks - K;  // for a reducer item
+    int64_t c = -1;                    // the chunk of this item, if any
+    if (item < nstatic) {
+      c = item;
+    } else if (item < nstatic + 2 * K) {
+      // A claim item: each of the 2K increments the counter once, so
+      // values 0 .. K-1 go to K distinct items and every tail chunk is
+      // taken exactly once; the item that makes the last increment returns
+      // the counter to zero, after which nothing in this launch touches it.
+      if (t == 0) {
+        const uint32_t v = __hip_atomic_fetch_add(&counters[kClaimCounter], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        if (v == (uint32_t)(2 * K - 1))
+          __hip_atomic_store(&counters[kClaimCounter], 0u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        claimed = v;
+      }
+      __syncthreads();
+      const uint32_t v = claimed;
+      __syncthreads();  // read by all before a later item writes it again
+      if (v >= (uint32_t)K) continue;  // the tail is gone
+      c = nstatic + v;
+    }
+    if (c >= 0) {
       // With kHold, the dx and dg stores of the chunk's last step are held
       // back until this wave's wait for its partial's store (below) is over:
       // that wait covers every store the wave has issued, and the freshest
@@ -963,7 +989,8 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                     (uint32_t)(st.dg / vec)};
   char* ws = static_cast<char*>(workspace);
   const int64_t tensor_bytes = rows * (int64_t)D * (16 / vec);
-  const int64_t nwork = L.nchunks + (deterministic && kReducers ? L.ngroups : 0);
+  const int64_t nwork = L.nchunks + claim_chunks(deterministic != 0, L.nchunks) +
+                       (deterministic && kReducers ? L.ngroups : 0);
   const int64_t grid = cap_grid(nwork, max_wg);
   return with_shape(dtype, D, [&](auto tt, auto dd) {
     constexpr Dt T = decltype(tt)::value;

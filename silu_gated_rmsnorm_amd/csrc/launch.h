@@ -38,6 +38,8 @@ constexpr int chunk_rows_for(int32_t row_bytes) {
 //   bytes [kNondetAccumByte, +nondet_slots(D)*8*D)
 //                                  the FP64 accumulators of the
 //                                  non-deterministic dw
+//   word  kClaimCounter            the tail-claim counter of the
+//                                  deterministic backward (claim_chunks)
 //   word  kOverallCounter          the overall counter (the last word)
 #ifndef GRN_COUNTER_WORDS
 #define GRN_COUNTER_WORDS 8192
@@ -63,6 +65,33 @@ constexpr int nondet_slots(int D) {
 }
 static_assert(nondet_slots(256) >= 1, "the non-deterministic accumulators fit");
 constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
+constexpr int kClaimCounter = kOverallCounter - 1;
+static_assert(kNondetAccumByte + nondet_slots(64) * 8 * 64 <= kClaimCounter * 4 &&
+                  kNondetAccumByte + nondet_slots(128) * 8 * 128 <= kClaimCounter * 4 &&
+                  kNondetAccumByte + nondet_slots(256) * 8 * 256 <= kClaimCounter * 4,
+              "the claim counter lies past the non-deterministic accumulators");
+
+// Chunks the deterministic backward hands out at run time (0: none).  The
+// grid's first nchunks - K items take chunk = item index; then come 2K
+// claim items, each taking the next of the last K chunks from an atomic
+// counter, or nothing once they are gone.  Workgroups are dealt to the 8
+// XCDs in index order, and the XCDs stream at rates a few per cent apart
+// (which one is slowest varies from run to run), so with static chunks
+// they finished 4-5 us apart at 7684x48 and 8-14 us at 32768x48; claim
+// items on an XCD that is ahead start sooner and take more of the tail.
+// Which workgroup runs a chunk does not change dw's bits.  Measured
+// (backward alone, BF16 D = 128, same process, alternating; static vs
+// K = 512): 7684x48 81.9 vs 81.0 us, 12296x48 126.8 vs 125.7, 16384x32
+// 112.8 vs 111.8, 32768x48 331.0 vs 327.6, 65536x48 669.4 vs 664.0,
+// 262144x48 2,746 vs 2,731; K = 256 gained less and K = 1024 lost up to
+// 2.7 %.  Below 2,048 chunks nothing is claimed.
+#ifndef GRN_BWD_CLAIM
+#define GRN_BWD_CLAIM 512
+#endif
+__host__ __device__ constexpr int64_t claim_chunks(bool det, int64_t nchunks) {
+  return (det && GRN_BWD_CLAIM > 0 && nchunks >= 4 * (int64_t)GRN_BWD_CLAIM) ? GRN_BWD_CLAIM
+                                                                              : 0;
+}
 
 struct BwdLayout {
   int64_t chunk_rows = 0;
