@@ -109,7 +109,10 @@ enum { GRN_DTYPE_BF16 = 0, GRN_DTYPE_F16 = 1, GRN_DTYPE_F32 = 2 };
 size_t gated_rmsnorm_workspace_bytes(int64_t rows, int32_t D);
 
 /* Rows R in one dw chunk of a backward over `rows` rows of D values of type
- * dtype: rows [c*R, (c+1)*R) form chunk c.  R depends only on the row size
+ * dtype (the workspace holds one partial per chunk; there are ceil(rows/R)
+ * chunks).  A chunk is a fixed set of R rows, made of equal blocks that
+ * may lie apart in the tensor (which rows form chunk c depends only on c,
+ * rows, D and dtype, never on the launch).  R depends only on the row size
  * in bytes (in this version 256 for 128-byte rows, i.e. D = 64 in BF16 or
  * FP16, and 128 otherwise, whatever `rows`); 0 for rows <= 0 or an
  * unsupported D or dtype. */
