@@ -8,9 +8,10 @@
 
 namespace grn {
 
-// Rows per dw chunk.  The backward adds the dw contributions of chunk
-// [c*R, (c+1)*R) into one FP32 partial, one workgroup per chunk; R, and
-// therefore the bits of dw, depend only on the row size.  R = 128 rows
+// Rows per dw chunk.  The backward adds the dw contributions of chunk c, a
+// fixed set of R rows (chunk_blocks() in kernels.hip says which), into one
+// FP32 partial, one workgroup per chunk.  R depends only on the row size;
+// the bits of dw depend only on rows, D and the type.  R = 128 rows
 // serves every row count (smaller chunks for small problems, 32 or 64 rows,
 // measured slower on MI355X: the extra partials and hand-offs cost more
 // than the added parallelism gains).  Rows of 128 bytes (D = 64 in a 16-bit
