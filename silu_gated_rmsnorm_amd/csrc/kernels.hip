@@ -36,6 +36,18 @@
 #ifndef GRN_FWD_LARGE_BYTES
 #define GRN_FWD_LARGE_BYTES (128ll << 20)
 #endif
+// Waves per forward workgroup, below and from GRN_FWD_LARGE_BYTES.
+// Measured (forward alone, graph-batched, same process, alternating; 4 vs 2
+// waves): 1031x48 9.02 vs 8.74 us, 2000x48 14.21 vs 13.99, 3534x48 22.81 vs
+// 22.45, 7684x48 46.36 vs 45.68, 10600x48 63.05 vs 62.05; with the 16-row
+// tiles 12296x48 71.8 vs 73.3 and 32768x48 186.9 vs 195.3.  One wave was no
+// better than two; eight and sixteen were slower.
+#ifndef GRN_FWD_WAVES
+#define GRN_FWD_WAVES 2
+#endif
+#ifndef GRN_FWD_WAVES_LARGE
+#define GRN_FWD_WAVES_LARGE 4
+#endif
 // Backward shape by tensor size (bytes of one [rows, D] activation):
 // row groups per wave step (U) and steps of loads prefetched ahead (PF).
 // From GRN_BWD_LARGE_BYTES up only some types and widths take the LARGE
@@ -200,8 +212,8 @@ __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
   }
 }
 
-template <Dt T, int D, int U>
-__global__ void __launch_bounds__(kBlock)
+template <Dt T, int D, int U, int kWaves>
+__global__ void __launch_bounds__(kWaves * kWave)
 fwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, u32x4* __restrict__ y, FwdPitch pt,
            int64_t rows, float eps, int64_t ntiles) {
@@ -210,9 +222,8 @@ fwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   const int lane = threadIdx.x & (kWave - 1);
   const u32x4 w_raw = w[lane & (S::kLanes - 1)];  // this lane's kVec values of w
 
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave_index();
-       t < ntiles; t += nwaves) {
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  for (int64_t t = (int64_t)blockIdx.x * kWaves + wave_index(); t < ntiles; t += nwaves) {
     const int64_t row0 = t * kTileRows;
     const u32x4* xb = x + row0 * pt.x;
     const u32x4* gb = g + row0 * pt.g;
@@ -880,9 +891,9 @@ constexpr int kFwdU = GRN_FWD_U;
 constexpr int kFwdULarge = GRN_FWD_U_LARGE;
 constexpr int kBwdWaves = GRN_BWD_WAVES;
 
-// A dispatch counts work-items in 32 bits, so a grid of 256-thread
-// workgroups stays below 2^24 of them; the kernels' grid-stride loops cover
-// any remaining work.
+// A dispatch counts work-items in 32 bits, so a grid of workgroups of at
+// most 256 threads stays below 2^24 of them; the kernels' grid-stride loops
+// cover any remaining work.
 constexpr int64_t kMaxGrid = (int64_t{1} << 24) - 1;
 
 int64_t cap_grid(int64_t want, int max_wg) {
@@ -957,21 +968,23 @@ hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
   return with_shape(dtype, D, [&](auto tt, auto dd) {
     constexpr Dt T = decltype(tt)::value;
     constexpr int DD = decltype(dd)::value;
-    auto launch = [&](auto u) {
+    auto launch = [&](auto u, auto waves) {
       constexpr int kU = decltype(u)::value;
+      constexpr int kW = decltype(waves)::value;
       constexpr int kTileRows = Shape<T, DD>::kRows * kU;
       const int64_t ntiles = (rows + kTileRows - 1) / kTileRows;
-      const int64_t want = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+      const int64_t want = (ntiles + kW - 1) / kW;
       const int64_t grid = cap_grid(want, max_wg);
-      hipLaunchKernelGGL((fwd_kernel<T, DD, kU>), dim3((unsigned)grid), dim3(kBlock), 0, s,
-                         static_cast<const u32x4*>(x), static_cast<const u32x4*>(g),
+      hipLaunchKernelGGL((fwd_kernel<T, DD, kU, kW>), dim3((unsigned)grid), dim3(kW * kWave), 0,
+                         s, static_cast<const u32x4*>(x), static_cast<const u32x4*>(g),
                          static_cast<const u32x4*>(w), static_cast<u32x4*>(y), pt, rows, eps,
                          ntiles);
     };
     if (large) {
-      launch(std::integral_constant<int, kFwdULarge>{});
+      launch(std::integral_constant<int, kFwdULarge>{},
+             std::integral_constant<int, GRN_FWD_WAVES_LARGE>{});
     } else {
-      launch(std::integral_constant<int, kFwdU>{});
+      launch(std::integral_constant<int, kFwdU>{}, std::integral_constant<int, GRN_FWD_WAVES>{});
     }
     return hipGetLastError();
   });
