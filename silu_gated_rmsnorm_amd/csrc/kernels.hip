@@ -36,6 +36,14 @@
 #ifndef GRN_FWD_LARGE_BYTES
 #define GRN_FWD_LARGE_BYTES (128ll << 20)
 #endif
+// ... up to tensors of this size, from which the 8-row tiles in two-wave
+// workgroups are faster again (forward alone, eager, same process: 16-row /
+// 8-row tiles 131072x48 797 / 786 us, 262144x48 1,619 / 1,572; 65536x48
+// 381 / 388; the step fwd + bwd 2,143 / 2,129, 4,347 / 4,301 and 1,024 /
+// 1,028 us).
+#ifndef GRN_FWD_HUGE_BYTES
+#define GRN_FWD_HUGE_BYTES (1ll << 30)
+#endif
 // Waves per forward workgroup, below and from GRN_FWD_LARGE_BYTES.
 // Measured (forward alone, graph-batched, same process, alternating; 4 vs 2
 // waves): 1031x48 9.02 vs 8.74 us, 2000x48 14.21 vs 13.99, 3534x48 22.81 vs
@@ -885,8 +893,9 @@ counters_zero_kernel(uint32_t* __restrict__ counters) {
 namespace {
 
 // Tile size of the forward by tensor size (results do not depend on it):
-// 4 row groups per tile stream large tensors faster (65536x48: 393 -> 378
-// us), 2 keep more waves in flight on small ones (1031x48: 9.4 -> 8.7 us).
+// 4 row groups per tile stream tensors of 128 MiB to 1 GiB faster (65536x48:
+// 393 -> 378 us), 2 keep more waves in flight on small ones (1031x48: 9.4
+// -> 8.7 us) and suit the largest (GRN_FWD_HUGE_BYTES).
 constexpr int kFwdU = GRN_FWD_U;
 constexpr int kFwdULarge = GRN_FWD_U_LARGE;
 constexpr int kBwdWaves = GRN_BWD_WAVES;
@@ -964,7 +973,9 @@ hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
   if (rows <= 0) return hipSuccess;
   const int vec = vec_of(dtype);
   const FwdPitch pt{(uint32_t)(st.x / vec), (uint32_t)(st.g / vec), (uint32_t)(st.y / vec)};
-  const bool large = rows * (int64_t)D * (16 / vec) >= (int64_t)GRN_FWD_LARGE_BYTES;
+  const int64_t tensor_bytes = rows * (int64_t)D * (16 / vec);
+  const bool large = tensor_bytes >= (int64_t)GRN_FWD_LARGE_BYTES &&
+                     tensor_bytes < (int64_t)GRN_FWD_HUGE_BYTES;
   return with_shape(dtype, D, [&](auto tt, auto dd) {
     constexpr Dt T = decltype(tt)::value;
     constexpr int DD = decltype(dd)::value;

@@ -161,11 +161,13 @@ def test_concurrent_streams():
             assert _same(x, y)
 
 
-def test_forward_tile_size_invariance():
-    """The forward picks a larger tile for tensors of 128 MiB and more; a
-    row's y must not depend on it: rows of a large call equal the same rows
-    computed in a small call, bit for bit."""
-    rows = 600000   # 153.6 MB per BF16 tensor: the large-tile path
+@pytest.mark.parametrize("rows", [600000, 4300000])
+def test_forward_tile_size_invariance(rows):
+    """The forward picks its tile and workgroup size by tensor size (16-row
+    tiles from 128 MiB, 8-row tiles again from 1 GiB); a row's y must not
+    depend on it: rows of a large call equal the same rows computed in a
+    small call, bit for bit.  600,000 rows are 146 MiB per BF16 tensor,
+    4,300,000 rows 1.03 GiB."""
     say(f"[determinism] forward tile size rows={rows}")
     inp = make_inputs(rows, seed=12, device="cuda")
     y_big = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
