@@ -15,8 +15,7 @@
 namespace grn {
 
 constexpr int kWave = 64;                            // CDNA wavefront
-constexpr int kBlock = 256;                          // threads per workgroup
-constexpr int kWavesPerBlock = kBlock / kWave;       // 4
+constexpr int kBlock = 256;                          // threads of the counter-zeroing kernel
 constexpr int kMaxD = 256;                           // widest supported row
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
