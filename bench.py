@@ -66,9 +66,10 @@ def counters_file(workload):
 # The deterministic backward kernel (template arguments: element type, D, row
 # groups per wave step, waves per workgroup, rows per chunk, prefetched
 # steps, deterministic, last step's stores held back, fence per work item,
-# window of chunks whose blocks interleave: 0 for the prefetching shape).
+# window of chunks whose blocks interleave: 0 for the prefetching shape,
+# recomputed forward fused in: only in the small checkpointed step).
 BWD_KERNEL = ("grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}, false, "
-              "{SWZ}>")
+              "{SWZ}, false>")
 KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
 
 

@@ -260,12 +260,17 @@ grn_status gated_rmsnorm_ckpt_step_strided(
   rs.dg = dg_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int max_wg = env_max_wg();
-  for (int pass = 0; pass < 2; ++pass) {
+  // Forward, then the recomputed forward and the backward: for small
+  // tensors the recomputed forward runs inside the backward's launch
+  // (grn::ckpt_fuses_forward), otherwise as a launch of its own.
+  const bool fuse = grn::ckpt_fuses_forward(rows, D, dtype, deterministic);
+  for (int pass = 0; pass < (fuse ? 1 : 2); ++pass) {
     if (grn::launch_fwd(x, g, w, y, rs, rows, D, dtype, eps, max_wg, s) != hipSuccess)
       return GRN_ERR_HIP;
   }
   return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, deterministic,
-                                    workspace, rs, rows, D, dtype, eps, max_wg, s));
+                                    workspace, rs, rows, D, dtype, eps, max_wg, s,
+                                    fuse ? y : nullptr));
 }
 
 grn_status gated_rmsnorm_ckpt_step(const void* x, const void* g,

@@ -677,7 +677,7 @@ constexpr bool prefetch_large() {
 #endif
 
 template <Dt T, int D, int U, int kWaves, int R, int kPrefetch, bool kDet, bool kHold,
-          bool kItemFence, int kSwz>
+          bool kItemFence, int kSwz, bool kFuseFwd>
 __global__ void __launch_bounds__(kWaves * kWave) GRN_BWD_OCCUPANCY
 bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            const u32x4* __restrict__ w, const u32x4* __restrict__ dy,
@@ -685,7 +685,8 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
            float* __restrict__ partial, float* __restrict__ gpart,
            uint32_t* __restrict__ counters, void* __restrict__ dw,
            int dw_fp32, int64_t rows, float eps, int64_t nchunks,
-           int64_t group_size, int64_t ngroups, int64_t cstride) {
+           int64_t group_size, int64_t ngroups, int64_t cstride,
+           u32x4* __restrict__ y, uint32_t ypitch, int64_t fwd_ntiles) {
   using S = Shape<T, D>;
   constexpr int kVec = S::kVec;
   constexpr int kThreads = kWaves * kWave;
@@ -746,7 +747,31 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   const int64_t nstatic = nchunks - K;
   const int64_t nwork = nchunks + K + (kDet && kReducers ? ngroups : 0);
   __shared__ uint32_t claimed;
-  for (int64_t item = blockIdx.x; item < nwork; item += gridDim.x) {
+  // kFuseFwd: after every backward item come the forward's tiles (the
+  // recomputed forward of the checkpointed step, which the backward does not
+  // read: it recomputes r from x), one 8-row-group tile per wave, so that
+  // they fill the slots the backward's last workgroups leave idle.
+  const int64_t nall = nwork + (kFuseFwd ? (fwd_ntiles + kWaves - 1) / kWaves : 0);
+  for (int64_t item = blockIdx.x; item < nall; item += gridDim.x) {
+    if constexpr (kFuseFwd) {
+      if (item >= nwork) {
+        constexpr int kFwdTileRows = S::kRows * 2;
+        const int64_t tile = (item - nwork) * kWaves + wave;
+        if (tile < fwd_ntiles) {
+          const FwdPitch fp{pt.x, pt.g, ypitch};
+          const int64_t row0 = tile * kFwdTileRows;
+          const u32x4 w_raw = w[col];
+          if (row0 + kFwdTileRows <= rows) {
+            fwd_tile<T, D, 2, true>(x + row0 * fp.x, g + row0 * fp.g, y + row0 * fp.y, fp,
+                                    w_raw, eps, lane, kFwdTileRows);
+          } else {
+            fwd_tile<T, D, 2, false>(x + row0 * fp.x, g + row0 * fp.g, y + row0 * fp.y, fp,
+                                     w_raw, eps, lane, (int)(rows - row0));
+          }
+        }
+        continue;
+      }
+    }
     // A compiler-only fence at the top of each work item (kItemFence): the
     // non-deterministic kernel then needs 184-205 VGPRs instead of 224-256
     // (two waves per SIMD instead of one at D = 256 and for FP32 at D =
@@ -1001,11 +1026,18 @@ hipError_t launch_fwd(const void* x, const void* g, const void* w, void* y,
   });
 }
 
+bool ckpt_fuses_forward(int64_t rows, int32_t D, int32_t dtype, int deterministic) {
+  const int64_t tensor_bytes = rows * (int64_t)D * (16 / vec_of(dtype));
+  return deterministic != 0 && rows > 0 && tensor_bytes < GRN_BWD_SMALL_BYTES;
+}
+
 hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
                       int dw_fp32, int deterministic, void* workspace,
                       const RowStrides& st, int64_t rows, int32_t D, int32_t dtype,
-                      float eps, int max_wg, hipStream_t s) {
+                      float eps, int max_wg, hipStream_t s, void* fused_y) {
+  if (fused_y != nullptr && !ckpt_fuses_forward(rows, D, dtype, deterministic))
+    return hipErrorInvalidValue;
   const int vec = vec_of(dtype);
   const BwdLayout L = bwd_layout(rows, D, 16 / vec);
   const BwdPitch pt{(uint32_t)(st.x / vec), (uint32_t)(st.g / vec),
@@ -1015,11 +1047,13 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
   const int64_t tensor_bytes = rows * (int64_t)D * (16 / vec);
   const int64_t nwork = L.nchunks + claim_chunks(deterministic != 0, L.nchunks) +
                        (deterministic && kReducers ? L.ngroups : 0);
-  const int64_t grid = cap_grid(nwork, max_wg);
   return with_shape(dtype, D, [&](auto tt, auto dd) {
     constexpr Dt T = decltype(tt)::value;
     constexpr int DD = decltype(dd)::value;
     constexpr int kR = chunk_rows_for(DD * 16 / Shape<T, DD>::kVec);
+    constexpr int kFwdTileRows = Shape<T, DD>::kRows * 2;
+    const int64_t fwd_ntiles = fused_y ? (rows + kFwdTileRows - 1) / kFwdTileRows : 0;
+    const int64_t grid = cap_grid(nwork + (fwd_ntiles + kBwdWaves - 1) / kBwdWaves, max_wg);
     if (L.nchunks == 0) {
       hipLaunchKernelGGL(dw_zero_kernel<T>, dim3(1), dim3(DD), 0, s, dw, dw_fp32);
       return hipGetLastError();
@@ -1032,7 +1066,8 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                          reinterpret_cast<float*>(ws + L.partial_off),
                          reinterpret_cast<float*>(ws + L.gpart_off),
                          reinterpret_cast<uint32_t*>(ws), dw, dw_fp32, rows, eps,
-                         L.nchunks, L.group_size, L.ngroups, L.counter_stride);
+                         L.nchunks, L.group_size, L.ngroups, L.counter_stride,
+                         static_cast<u32x4*>(fused_y), (uint32_t)(st.y / vec), fwd_ntiles);
     };
     // Shapes measured fastest per size (1031x48 is "small", 7684x48 and up
     // "mid"; tensors of 256 MiB and more take the prefetching shape only
@@ -1041,20 +1076,25 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
     if (!deterministic) {
       if (tensor_bytes < GRN_BWD_LARGE_BYTES) {
         launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
-                          true, GRN_BWD_SWZ>);
+                          true, GRN_BWD_SWZ, false>);
       } else {
         launch(bwd_kernel<T, DD, GRN_BWD_U_ND, kBwdWaves, kR, GRN_BWD_ND_PREFETCH, false, false,
-                          false, GRN_BWD_SWZ>);
+                          false, GRN_BWD_SWZ, false>);
       }
     } else if (tensor_bytes < GRN_BWD_SMALL_BYTES) {
-      launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false,
-                        false, GRN_BWD_SWZ>);
+      if (fused_y != nullptr) {
+        launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false,
+                          false, GRN_BWD_SWZ, true>);
+      } else {
+        launch(bwd_kernel<T, DD, GRN_BWD_U_SMALL, kBwdWaves, kR, GRN_BWD_PF_SMALL, true, false,
+                          false, GRN_BWD_SWZ, false>);
+      }
     } else if (tensor_bytes < GRN_BWD_LARGE_BYTES || !prefetch_large<T, DD>()) {
       launch(bwd_kernel<T, DD, GRN_BWD_U_MID, kBwdWaves, kR, GRN_BWD_PF_MID, true, false,
-                        false, GRN_BWD_SWZ>);
+                        false, GRN_BWD_SWZ, false>);
     } else {
       launch(bwd_kernel<T, DD, GRN_BWD_U_LARGE, kBwdWaves, kR, GRN_BWD_PF_LARGE, true,
-                        hold_large<T, DD>(), false, 0>);
+                        hold_large<T, DD>(), false, 0, false>);
     }
     return hipGetLastError();
   });

@@ -127,7 +127,17 @@ hipError_t launch_bwd(const void* x, const void* g, const void* w,
                       const void* dy, void* dx, void* dg, void* dw,
                       int dw_fp32, int deterministic, void* workspace,
                       const RowStrides& st, int64_t rows, int32_t D, int32_t dtype,
-                      float eps, int max_wg, hipStream_t s);
+                      float eps, int max_wg, hipStream_t s, void* fused_y = nullptr);
+
+// Whether the checkpointed step runs its recomputed forward inside the
+// backward's launch (launch_bwd with fused_y = y): for the deterministic dw
+// and tensors below 32 MiB, whose backward runs as one round of workgroups.
+// Measured (checkpointed step, same process, alternating; separate vs
+// fused): 1031x48 32.0 vs 27.9 us, 1500x48 42.8 vs 37.0, 2000x48 48.9 vs
+// 47.6, 2600x48 63.1 vs 59.7; from 41 MiB up the forward's tiles, run at the
+// backward's occupancy, made the step slower (3534x48 83.6 vs 84.9,
+// 7684x48 160.3 vs 175.0).  Every output bit is the same either way.
+bool ckpt_fuses_forward(int64_t rows, int32_t D, int32_t dtype, int deterministic);
 
 hipError_t launch_counters_zero(void* workspace, hipStream_t s);
 

@@ -74,8 +74,10 @@ def test_launch_shape_invariance(rows, monkeypatch):
 
 
 @pytest.mark.parametrize("dw_fp32", [True, False])
-def test_ckpt_step_equals_fwd_then_bwd(dw_fp32):
-    rows = 9999
+@pytest.mark.parametrize("rows", [9999, 200000])
+def test_ckpt_step_equals_fwd_then_bwd(dw_fp32, rows):
+    """9,999 rows run the recomputed forward inside the backward's launch
+    (small tensors), 200,000 rows (49 MiB) as a launch of its own."""
     say(f"[determinism] ckpt vs fwd+bwd rows={rows} dw_fp32={dw_fp32}")
     inp = make_inputs(rows, seed=5, device="cuda")
     y1 = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
