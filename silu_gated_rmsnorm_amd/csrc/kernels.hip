@@ -749,8 +749,9 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
   __shared__ uint32_t claimed;
   // kFuseFwd: after every backward item come the forward's tiles (the
   // recomputed forward of the checkpointed step, which the backward does not
-  // read: it recomputes r from x), one 8-row-group tile per wave, so that
-  // they fill the slots the backward's last workgroups leave idle.
+  // read: it recomputes r from x), one tile of two row groups per wave (the
+  // forward's tile below 128 MiB), so that they fill the slots the
+  // backward's last workgroups leave idle.
   const int64_t nall = nwork + (kFuseFwd ? (fwd_ntiles + kWaves - 1) / kWaves : 0);
   for (int64_t item = blockIdx.x; item < nall; item += gridDim.x) {
     if constexpr (kFuseFwd) {
