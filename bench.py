@@ -70,7 +70,17 @@ def counters_file(workload):
 # recomputed forward fused in: only in the small checkpointed step).
 BWD_KERNEL = ("grn::bwd_kernel<(grn::Dt){code}, {D}, {U}, 4, {R}, {PF}, true, {HOLD}, false, "
               "{SWZ}, false>")
-KERNEL_SOURCE = ROOT / "silu_gated_rmsnorm_amd" / "csrc" / "kernels.hip"
+# The sources the kernels are compiled from: the committed HBM counter
+# figures apply only while their combined SHA-256 is the one recorded.
+KERNEL_SOURCES = tuple(ROOT / "silu_gated_rmsnorm_amd" / "csrc" / name
+                       for name in ("kernels.hip", "common.h", "launch.h"))
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(path.read_bytes())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -446,8 +456,7 @@ def traffic_from_counters(workload):
         return None
     if rec.get("workload") != workload:
         return None
-    sha = hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -510,8 +519,7 @@ def summarize_counters(fetch_csv, write_csv, workload="7684x48"):
                         "hbm_bytes_per_launch": round(rd + wr),
                         "algorithmic_bytes": alg[key],
                         "traffic_over_algorithmic": round((rd + wr) / alg[key], 4)}
-    sha = hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
-    rec = {"workload": workload, "kernel_source_sha256": sha,
+    rec = {"workload": workload, "kernel_source_sha256": kernel_source_sha(),
            "copy_bytes": copy_bytes, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
            "copy_dispatches": [ncf, ncw],
            "fetch_scale": round(scale_f, 6), "write_scale": round(scale_w, 6),

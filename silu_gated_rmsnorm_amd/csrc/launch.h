@@ -85,13 +85,17 @@ static_assert(kNondetAccumByte + nondet_slots(64) * 8 * 64 <= kClaimCounter * 4 
 // K = 512): 7684x48 81.9 vs 81.0 us, 12296x48 126.8 vs 125.7, 16384x32
 // 112.8 vs 111.8, 32768x48 331.0 vs 327.6, 65536x48 669.4 vs 664.0,
 // 262144x48 2,746 vs 2,731; K = 256 gained less and K = 1024 lost up to
-// 2.7 %.  Below 2,048 chunks nothing is claimed.
+// 2.7 %.  Grids of 1,024 to 2,047 chunks claim 256 (3534x48 43.6 vs 43.2
+// us, 5000x48 56.7 vs 56.3, BF16 D = 64 at 7684x48 rows 45.2 vs 44.9);
+// smaller grids, which run as about one round of workgroups, claim none.
 #ifndef GRN_BWD_CLAIM
 #define GRN_BWD_CLAIM 512
 #endif
 __host__ __device__ constexpr int64_t claim_chunks(bool det, int64_t nchunks) {
-  return (det && GRN_BWD_CLAIM > 0 && nchunks >= 4 * (int64_t)GRN_BWD_CLAIM) ? GRN_BWD_CLAIM
-                                                                              : 0;
+  return (!det || GRN_BWD_CLAIM <= 0)                  ? 0
+         : nchunks >= 4 * (int64_t)GRN_BWD_CLAIM      ? GRN_BWD_CLAIM
+         : nchunks >= 2 * (int64_t)GRN_BWD_CLAIM      ? GRN_BWD_CLAIM / 2
+                                                      : 0;
 }
 
 struct BwdLayout {

@@ -36,7 +36,9 @@ def _write_csv(path, counter, rows):
 def counters(tmp_path, monkeypatch):
     src = tmp_path / "kernels.hip"
     src.write_text("// kernel source v1\n")
-    monkeypatch.setattr(bench, "KERNEL_SOURCE", src)
+    hdr = tmp_path / "launch.h"
+    hdr.write_text("// header v1\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", (src, hdr))
     monkeypatch.setattr(bench, "PROFILES_DIR", tmp_path)
     from silu_gated_rmsnorm_amd.inputs import WORKLOADS
     rows = WORKLOADS["1031x48"].rows
@@ -53,7 +55,7 @@ def counters(tmp_path, monkeypatch):
     _write_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch_rows)
     _write_csv(tmp_path / "w.csv", "WRITE_SIZE", write_rows)
     bench.summarize_counters(tmp_path / "f.csv", tmp_path / "w.csv", workload="1031x48")
-    return {"src": src, "copy": copy, "rows": rows,
+    return {"src": src, "hdr": hdr, "copy": copy, "rows": rows,
             "rec": json.loads((tmp_path / "bwd_kernel_1031x48_traffic.json").read_text())}
 
 
@@ -75,5 +77,9 @@ def test_scaling(counters):
 def test_traffic_applies_only_to_its_workload_and_source(counters):
     assert bench.traffic_from_counters("1031x48") == 5 * counters["copy"]
     assert bench.traffic_from_counters("7684x48") is None   # no file for it here
+    counters["hdr"].write_text("// header v2\n")    # any kernel source counts
+    assert bench.traffic_from_counters("1031x48") is None
+    counters["hdr"].write_text("// header v1\n")
+    assert bench.traffic_from_counters("1031x48") == 5 * counters["copy"]
     counters["src"].write_text("// kernel source v2\n")
     assert bench.traffic_from_counters("1031x48") is None
