@@ -90,6 +90,31 @@ def test_ckpt_step_equals_fwd_then_bwd(dw_fp32, rows):
         assert _same(a, b)
 
 
+def test_ckpt_step_fused_with_tail_claims():
+    """FP32 rows of D = 64 are 256 bytes: 131,071 rows stay below 32 MiB per
+    tensor (the recomputed forward runs inside the backward's launch) and
+    make 1,024 chunks (the backward claims its last 256 at run time), so one
+    launch holds backward items, claim items, reducer items and forward
+    tiles.  The step must equal fwd then bwd bit for bit, twice in a row on
+    one workspace (the claim counter returns to zero)."""
+    rows, D = 131071, 64
+    say(f"[determinism] fused ckpt with tail claims rows={rows} D={D} FP32")
+    inp = make_inputs(rows, D, seed=13, device="cuda", dtype=torch.float32)
+    y1 = binding.gated_rmsnorm_fwd(inp["x"], inp["g"], inp["w"], 1e-6)
+    dx1, dg1, dw1 = binding.gated_rmsnorm_bwd(inp["x"], inp["g"], inp["w"], inp["dy"], 1e-6,
+                                              dw_fp32=True)
+    ws = binding.new_workspace(rows, "cuda", D=D)
+    for _ in range(2):
+        y2, dx2, dg2, dw2 = binding.gated_rmsnorm_ckpt_step(inp["x"], inp["g"], inp["w"],
+                                                            inp["dy"], 1e-6, dw_fp32=True,
+                                                            workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in ((y1, y2), (dx1, dx2), (dg1, dg2), (dw1, dw2)):
+            assert _same(a, b)
+    C = binding.load_library().gated_rmsnorm_workspace_init_bytes()
+    assert torch.count_nonzero(ws[:C]).item() == 0
+
+
 def test_workspace_reused_across_sizes():
     """The counters return to zero after each call: one workspace serves
     calls of different sizes in any order, with the same bits as fresh ones.
