@@ -147,10 +147,15 @@ grn_status gated_rmsnorm_bwd(const void *x, const void *g, const void *w,
                              int32_t dtype, int32_t dw_fp32, void *stream);
 
 /* The checkpointed training step: forward, forward again (recompute, into
- * the same y), then the backward, enqueued in that order on `stream`.
- * Arguments are those of gated_rmsnorm_fwd and gated_rmsnorm_bwd together;
- * y must not overlap any other buffer.  Outputs are bitwise those of
- * gated_rmsnorm_fwd followed by gated_rmsnorm_bwd. */
+ * the same y), then the backward, enqueued on `stream` (flashinfer PR #8701,
+ * "How the tables were measured": 2 x forward + backward).  The backward
+ * reads x, g, dy and w, not y, so the recomputed forward may run inside the
+ * backward's launch (this version does so for the deterministic dw and
+ * tensors below 32 MiB); either way both forwards have completed when the
+ * stream reaches the next operation.  Arguments are those of
+ * gated_rmsnorm_fwd and gated_rmsnorm_bwd together; y must not overlap any
+ * other buffer.  Outputs are bitwise those of gated_rmsnorm_fwd followed by
+ * gated_rmsnorm_bwd. */
 grn_status gated_rmsnorm_ckpt_step(const void *x, const void *g,
                                    const void *w, const void *dy, void *y,
                                    void *dx, void *dg, void *dw,
