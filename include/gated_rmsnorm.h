@@ -35,7 +35,11 @@
  *  - dtype: the element type of every activation and of w: GRN_DTYPE_BF16
  *    (the type the pages measure), GRN_DTYPE_F16 or GRN_DTYPE_F32.
  *    Arithmetic is FP32; each BF16/FP16 output is rounded once, to nearest
- *    even (FP16 results beyond its range become infinite).
+ *    even (FP16 results beyond its range become infinite).  Any finite
+ *    input is in range: a row whose sum of squares exceeds FP32 (entries
+ *    beyond about 1.8e19) is summed again over x scaled by 2^-70.  With
+ *    eps = 0 (or below about 1e-37), rows whose mean square falls below
+ *    FP32's smallest normal number (about 1.2e-38) lose accuracy.
  *  - D: 64, 128 or 256 (the pages measure D = 128).
  *  - rows: 0 <= rows <= GRN_MAX_ROWS.  rows = 0 is allowed: the forward does
  *    nothing, the backward writes dw = 0 (an empty sum).  Activation pointers
@@ -63,6 +67,11 @@
  *  - Launch shape: the environment variable GATED_RMSNORM_MAX_WG, when set
  *    to a positive integer, caps the number of workgroups per launch (a
  *    tuning and testing knob).  Results do not depend on it.
+ *  - Testing knob: GATED_RMSNORM_CKPT_SKIP_FIRST_FWD, when set to anything
+ *    but "" or "0", makes gated_rmsnorm_ckpt_step(_strided) skip its first
+ *    forward, so that y is written by the recomputed forward alone (which
+ *    may run inside the backward's launch).  Every output keeps its value;
+ *    only which launch writes y changes.
  */
 #ifndef GATED_RMSNORM_H
 #define GATED_RMSNORM_H

@@ -66,6 +66,15 @@ int env_max_wg() {
   return static_cast<int>(v);
 }
 
+// Test knob: a set, non-empty GATED_RMSNORM_CKPT_SKIP_FIRST_FWD (other than
+// "0") makes the checkpointed step skip its first forward, so that y comes
+// from the recomputed forward alone (inside the backward's launch where the
+// step fuses them).
+bool env_skip_first_fwd() {
+  const char* s = std::getenv("GATED_RMSNORM_CKPT_SKIP_FIRST_FWD");
+  return s != nullptr && *s != '\0' && !(s[0] == '0' && s[1] == '\0');
+}
+
 grn_status check_common(int64_t rows, int32_t D, int32_t dtype) {
   if (!supported_d(D) || rows < 0 || rows > GRN_MAX_ROWS) return GRN_ERR_SHAPE;
   if (!supported_dtype(dtype)) return GRN_ERR_DTYPE;
@@ -264,7 +273,7 @@ grn_status gated_rmsnorm_ckpt_step_strided(
   // tensors the recomputed forward runs inside the backward's launch
   // (grn::ckpt_fuses_forward), otherwise as a launch of its own.
   const bool fuse = grn::ckpt_fuses_forward(rows, D, dtype, deterministic);
-  for (int pass = 0; pass < (fuse ? 1 : 2); ++pass) {
+  for (int pass = env_skip_first_fwd() ? 1 : 0; pass < (fuse ? 1 : 2); ++pass) {
     if (grn::launch_fwd(x, g, w, y, rs, rows, D, dtype, eps, max_wg, s) != hipSuccess)
       return GRN_ERR_HIP;
   }

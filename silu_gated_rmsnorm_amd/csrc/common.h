@@ -173,4 +173,26 @@ __device__ __forceinline__ float rsqrt_fast(float v) {
   return __builtin_amdgcn_rsqf(v);
 }
 
+// Rows whose sum of squares exceeds the FP32 range (entries beyond about
+// 1.8e19 at D = 128; BF16 and FP32 storage hold values up to 3.4e38, while
+// FP16's largest, 65504, squares to far less) are summed again with every x
+// scaled by kOverflowScale = 2^-70, an exact power of two: the scaled
+// squares of up to 256 entries of at most 3.4e38 stay below 2^124, and the
+// largest entry of such a row (at least 2^60) keeps its scaled square far
+// above FP32's underflow.  With x' = 2^-70 x:
+//   mean(x^2) + eps = 2^140 (mean(x'^2) + 2^-140 eps)
+//   r = 2^-70 r',  r' = rsqrt(mean(x'^2) + 2^-140 eps)
+//   mean(dn n) = r' mean(dn x')
+constexpr float kOverflowScale = 0x1p-70f;
+constexpr float kOverflowScale2 = 0x1p-140f;
+
+// Whether a row sum of squares is not a finite FP32 number (+inf, or NaN
+// from a NaN or infinite input).
+__device__ __forceinline__ bool overflowed(float ss) { return !(ss <= 0x1.fffffep127f); }
+
+// Whether some lane of the wave holds a NaN in v (wave-uniform).
+__device__ __forceinline__ bool wave_any_nan(float v) {
+  return __builtin_amdgcn_ballot_w64(v != v) != 0;
+}
+
 }  // namespace grn

@@ -20,6 +20,9 @@
 // operations) is not negligible next to its memory time, so it is kept
 // lean: shared products, wave-uniform (scalar) addressing, and no per-lane
 // predicates except in the one tile that holds the ragged end of the rows.
+// Rows whose sum of squares overflows FP32 are marked (r becomes NaN) at
+// the cost of two instructions and redone by a cold fix-up pass that the
+// wave enters only when it saw such a row (fwd_tile, bwd_chunk_fixup).
 #include "common.h"
 #include "launch.h"
 
@@ -167,6 +170,16 @@ __device__ __forceinline__ uint32_t lane_offset(int lane, int u, uint32_t pitch)
          (uint32_t)(lane & (S::kLanes - 1));
 }
 
+// The same offset as a signed 64-bit value, for the backward's fix-up pass
+// (bwd_chunk): had the fix-up used lane_offset's unsigned 32-bit form, which
+// the main pass needs for its scalar-base addressing, the compiler would have
+// shared that form between the two and given the whole kernel 256 VGPRs.
+template <class S>
+__device__ __forceinline__ int64_t lane_offset_cold(int lane, int u, uint32_t pitch) {
+  return (int64_t)(S::kRows * u + lane / S::kLanes) * (int64_t)pitch +
+         (int64_t)(lane & (S::kLanes - 1));
+}
+
 // --------------------------------------------------------------------------
 // Forward.  A wave tile is U groups of kRows consecutive rows.  Lane l owns
 // values [kVec(l%kLanes), kVec(l%kLanes)+kVec) of tile row kRows*u +
@@ -176,6 +189,60 @@ __device__ __forceinline__ uint32_t lane_offset(int lane, int u, uint32_t pitch)
 struct FwdPitch {
   uint32_t x, g, y;  // row pitches in 16-byte units
 };
+
+// Whether a row's sum of squares can exceed FP32's range: not for FP16
+// storage (its largest square, 65504^2, times 256 entries is about 1.1e12).
+template <Dt T, int D>
+constexpr bool can_overflow() {
+  return T != Dt::f16;
+}
+
+// y for one row group of a forward tile (lane l: row kRows*u + l/kLanes).
+// The main pass (kFix = false) marks a row whose sum of squares overflowed
+// FP32 by making its r NaN (r times fma(ss, 0, 1): exactly 1 for a finite
+// sum), so its y comes out NaN and so does `mark`.  The fix-up pass (kFix =
+// true) takes the sum again over x scaled by kOverflowScale and stores y of
+// those rows only.
+template <Dt T, int D, bool kFix>
+__device__ __forceinline__ void fwd_rows(u32x4 xv, u32x4 gv, u32x4* __restrict__ dst,
+                                         const float (&wf)[Shape<T, D>::kVec], float eps,
+                                         bool valid, float& mark) {
+  using S = Shape<T, D>;
+  using C = typename S::C;
+  constexpr int kVec = S::kVec;
+  float xf[kVec], gf[kVec];
+  C::unpack(xv, xf);
+  C::unpack(gv, gf);
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) ss = fmaf(xf[e], xf[e], ss);
+  ss = row_sum<S::kLanes>(ss);
+  float r = rsqrt_fast(ss * (1.0f / D) + eps);
+  bool fix_row = false;
+  if constexpr (!kFix) {
+    if constexpr (can_overflow<T, D>()) {
+      r *= fmaf(ss, 0.0f, 1.0f);
+      mark += r;
+    }
+  } else {
+    float ss2 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const float xs = xf[e] * kOverflowScale;
+      ss2 = fmaf(xs, xs, ss2);
+    }
+    ss2 = row_sum<S::kLanes>(ss2);
+    fix_row = overflowed(ss);
+    r = rsqrt_fast(ss2 * (1.0f / D) + eps * kOverflowScale2) * kOverflowScale;
+  }
+  float yf[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    const float s = gf[e] * sigmoid_fast(gf[e]);
+    yf[e] = (xf[e] * r) * wf[e] * s;
+  }
+  if (valid && (!kFix || fix_row)) st_stream<(GRN_FWD_NTS & 1) != 0>(dst, C::pack(yf));
+}
 
 template <Dt T, int D, int U, bool kFull>
 __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
@@ -199,24 +266,32 @@ __device__ __forceinline__ void fwd_tile(const u32x4* __restrict__ xb,
   }
   float wf[kVec];
   C::unpack(use_when_needed(w_raw), wf);
+  float mark = 0.0f;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float xf[kVec], gf[kVec];
-    C::unpack(xv[u], xf);
-    C::unpack(gv[u], gf);
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) ss = fmaf(xf[e], xf[e], ss);
-    ss = row_sum<S::kLanes>(ss);
-    const float r = rsqrt_fast(ss * (1.0f / D) + eps);
-    float yf[kVec];
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const float s = gf[e] * sigmoid_fast(gf[e]);
-      yf[e] = (xf[e] * r) * wf[e] * s;
+  for (int u = 0; u < U; ++u)
+    fwd_rows<T, D, false>(xv[u], gv[u], yb + lane_offset<S>(lane, u, pt.y), wf, eps,
+                          kFull || S::kRows * u + sub < nvalid, mark);
+  // A row whose sum of squares overflowed FP32 (entries beyond ~1.8e19 at
+  // D = 128): its y went out NaN; store it again from the scaled sum (the
+  // same address, later in the same lane's program order).  Taken by no
+  // wave on data within FP32's range.
+  if (can_overflow<T, D>() && wave_any_nan(mark)) {
+    // Opaque copies (as in the backward's fix-up): nothing here is hoisted
+    // into, or shared with, the main pass.
+    int cl = lane;
+    FwdPitch cp = pt;
+    asm volatile("" : "+v"(cl), "+s"(cp.x), "+s"(cp.g), "+s"(cp.y));
+    const int csub = cl / S::kLanes;
+#pragma unroll 1
+    for (int u = 0; u < U; ++u) {
+      const bool valid = kFull || S::kRows * u + csub < nvalid;
+      u32x4 xr = u32x4{0, 0, 0, 0}, gr = u32x4{0, 0, 0, 0};
+      if (valid) {
+        xr = xb[lane_offset_cold<S>(cl, u, cp.x)];
+        gr = gb[lane_offset_cold<S>(cl, u, cp.g)];
+      }
+      fwd_rows<T, D, true>(xr, gr, yb + lane_offset_cold<S>(cl, u, cp.y), wf, eps, valid, mark);
     }
-    if (kFull || S::kRows * u + sub < nvalid)
-      st_stream<(GRN_FWD_NTS & 1) != 0>(yb + lane_offset<S>(lane, u, pt.y), C::pack(yf));
   }
 }
 
@@ -298,7 +373,22 @@ __device__ __forceinline__ void bwd_load(BwdRaw<U>& r,
   }
 }
 
-template <Dt T, int D, int U, bool kFull, bool kDefer>
+// One wave step of the backward.
+//
+// Rows whose sum of squares overflows FP32 (entries beyond about 1.8e19 at
+// D = 128) need the sums taken over scaled x (kOverflowScale).  A branch
+// inside the unrolled step, however rarely taken, made the compiler keep
+// every row group's values live across it (256 VGPRs: one wave per SIMD
+// instead of two or three), and so did any per-row flag carried through
+// the steps.  So the main pass (kFix = false) marks such a row by making
+// its r NaN instead (r times fma(ss, 0, 1), which is exactly 1 for a finite
+// sum and NaN for an infinite one: two instructions, no live state); the
+// NaN reaches the lane's dw accumulator, which bwd_chunk tests once per
+// chunk.  The fix-up pass (kFix = true) recomputes a wave's steps: every
+// row's dw term again, in the main pass's order (the same bits for the
+// other rows), and for the overflowed rows the scaled sums, whose dx and dg
+// it writes over the main pass's NaN.
+template <Dt T, int D, int U, bool kFull, bool kDefer, bool kFix = false>
 __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
                                             u32x4* __restrict__ dxb,
                                             u32x4* __restrict__ dgb, BwdPitch pt,
@@ -334,8 +424,31 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
     }
     ss = row_sum<S::kLanes>(ss);
     sd = row_sum<S::kLanes>(sd);
-    const float rs = rsqrt_fast(ss * (1.0f / D) + eps);
-    const float cr = rs * sd * (1.0f / D);  // c = mean(dn n) = r mean(dn x)
+    float rs = rsqrt_fast(ss * (1.0f / D) + eps);
+    float cr;
+    bool fix_row = false;
+    if constexpr (!kFix) {
+      if constexpr (can_overflow<T, D>())
+        rs *= fmaf(ss, 0.0f, 1.0f);  // NaN marks a row beyond FP32's range
+      cr = rs * sd * (1.0f / D);   // c = mean(dn n) = r mean(dn x)
+    } else {
+      cr = rs * sd * (1.0f / D);
+      // Both sums again over x scaled by 2^-70 (exact), which also keeps
+      // sum(dn x) of such rows in range; used for overflowed rows only.
+      float ss2 = 0.0f, sd2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float xs = xf[e] * kOverflowScale;
+        ss2 = fmaf(xs, xs, ss2);
+        sd2 = fmaf(dn[e], xs, sd2);
+      }
+      ss2 = row_sum<S::kLanes>(ss2);
+      sd2 = row_sum<S::kLanes>(sd2);
+      const float rs2 = rsqrt_fast(ss2 * (1.0f / D) + eps * kOverflowScale2);
+      fix_row = overflowed(ss);
+      rs = fix_row ? rs2 * kOverflowScale : rs;
+      cr = fix_row ? rs2 * sd2 * (1.0f / D) : cr;
+    }
     float dxf[kVec], dgf[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
@@ -344,15 +457,23 @@ __device__ __forceinline__ void bwd_compute(const BwdRaw<U>& r,
       dgf[e] = tg[e] * n;
       q[e] *= n;  // dw contribution dy n s
     }
-    if (kFull || S::kRows * u + sub < nvalid) {
-      if constexpr (kDefer) {
-        // Packed here, not where they are stored: the opaque copies keep
-        // the compiler from carrying the FP32 values to the stores.
-        held.dx[u] = use_when_needed(C::pack(dxf));
-        held.dg[u] = use_when_needed(C::pack(dgf));
-      } else {
-        st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), C::pack(dxf));
-        st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), C::pack(dgf));
+    const bool valid = kFull || S::kRows * u + sub < nvalid;
+    if (valid) {
+      if (!kFix || fix_row) {
+        if constexpr (kDefer) {
+          // Packed here, not where they are stored: the opaque copies keep
+          // the compiler from carrying the FP32 values to the stores.
+          held.dx[u] = use_when_needed(C::pack(dxf));
+          held.dg[u] = use_when_needed(C::pack(dgf));
+        } else if constexpr (kFix) {
+          st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset_cold<S>(lane, u, pt.dx),
+                                            C::pack(dxf));
+          st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset_cold<S>(lane, u, pt.dg),
+                                            C::pack(dgf));
+        } else {
+          st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), C::pack(dxf));
+          st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), C::pack(dgf));
+        }
       }
 #pragma unroll
       for (int e = 0; e < kVec; ++e) acc[e] += q[e];
@@ -374,6 +495,56 @@ __device__ __forceinline__ void bwd_store_held(const BwdOut<U>& held,
     if (kFull || S::kRows * u + sub < held.nvalid) {
       st_stream<(GRN_BWD_NTS & 1) != 0>(dxb + lane_offset<S>(lane, u, pt.dx), held.dx[u]);
       st_stream<(GRN_BWD_NTS & 2) != 0>(dgb + lane_offset<S>(lane, u, pt.dg), held.dg[u]);
+    }
+  }
+}
+
+// The backward's fix-up of one wave's share of a chunk, for a wave whose
+// dw accumulator came out NaN: some row's sum of squares overflowed FP32 (or
+// the inputs hold a NaN or an infinity).  The wave reads its steps again,
+// one row group at a time, and redoes them in the main pass's order
+// (bwd_compute, kFix): dw's bits are those of a pass that had summed those
+// rows right the first time.  Its stores go to the same addresses as the main
+// pass's, later in the same lane's program order.  Kept out of line: inlined,
+// its address arithmetic changed how the compiler allocated the main pass's
+// registers (256 VGPRs, one wave per SIMD).
+template <Dt T, int D, int U, int kWaves, int R, bool kHold, bool kFull>
+__device__ __forceinline__ void bwd_chunk_fixup(
+    const u32x4* __restrict__ x, const u32x4* __restrict__ g, const u32x4* __restrict__ dy,
+    u32x4* __restrict__ dx, u32x4* __restrict__ dg, BwdPitch pt,
+    const float (&wf)[Shape<T, D>::kVec], float eps, int64_t chunk0, int64_t it_stride,
+    int64_t rows, int wave, int lane, float (&acc)[Shape<T, D>::kVec], BwdOut<U>& held) {
+  using S = Shape<T, D>;
+  constexpr int kRows = S::kRows;
+  constexpr int kStepRows = kRows * U;
+  constexpr int kIters = R / (kWaves * kStepRows);
+  asm volatile("" : "+v"(lane), "+s"(pt.x), "+s"(pt.g), "+s"(pt.dy), "+s"(pt.dx), "+s"(pt.dg));
+#pragma unroll
+  for (int e = 0; e < S::kVec; ++e) acc[e] = 0.0f;
+#pragma unroll 1
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t row0 = chunk0 + it * it_stride + (int64_t)wave * kStepRows;
+    const int64_t left = rows - row0;
+    const int nvalid = (int)(left < 0 ? 0 : (left > kStepRows ? kStepRows : left));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r0 = row0 + kRows * u;
+      const int nv = nvalid - kRows * u;
+      BwdRaw<1> b;
+      BwdOut<1> h;
+      bwd_load<S, 1, kFull>(b, x + r0 * pt.x, g + r0 * pt.g, dy + r0 * pt.dy, pt, lane, nv);
+      if (kHold && it + 1 == kIters) {
+        // this step's stores are still held: patch the held values
+        h.dx[0] = held.dx[u];
+        h.dg[0] = held.dg[u];
+        bwd_compute<T, D, 1, kFull, true, true>(b, dx + r0 * pt.dx, dg + r0 * pt.dg, pt, wf,
+                                                eps, lane, nv, acc, h);
+        held.dx[u] = h.dx[0];
+        held.dg[u] = h.dg[0];
+      } else {
+        bwd_compute<T, D, 1, kFull, false, true>(b, dx + r0 * pt.dx, dg + r0 * pt.dg, pt, wf,
+                                                 eps, lane, nv, acc, h);
+      }
     }
   }
 }
@@ -439,46 +610,78 @@ __device__ __forceinline__ void bwd_chunk(const u32x4* __restrict__ x,
         asm volatile("" ::: "memory");  // and the stores before the next step
       }
     }
-    return;
-  }
-  // A ring of kDepth register buffers: step it+kDepth-1 is loaded while
-  // step it is computed.
-  constexpr int kDepth = kPrefetch + 1;
-  BwdRaw<U> buf[kDepth];
-  auto load = [&](BwdRaw<U>& b, int it) {
-    const int64_t row0 = row_of(it);
-    bwd_load<S, U, kFull>(b, x + row0 * pt.x, g + row0 * pt.g, dy + row0 * pt.dy, pt,
-                          lane, nvalid_of(it));
-  };
+  } else {
+    // A ring of kDepth register buffers: step it+kDepth-1 is loaded while
+    // step it is computed.
+    constexpr int kDepth = kPrefetch + 1;
+    BwdRaw<U> buf[kDepth];
+    auto load = [&](BwdRaw<U>& b, int it) {
+      const int64_t row0 = row_of(it);
+      bwd_load<S, U, kFull>(b, x + row0 * pt.x, g + row0 * pt.g, dy + row0 * pt.dy, pt,
+                            lane, nvalid_of(it));
+    };
 #pragma unroll
-  for (int k = 0; k < kDepth - 1; ++k) {
-    if (k < kIters) load(buf[k], k);
-  }
+    for (int k = 0; k < kDepth - 1; ++k) {
+      if (k < kIters) load(buf[k], k);
+    }
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int ahead = it + kDepth - 1;
-    if (ahead < kIters) load(buf[ahead % kDepth], ahead);
-    const int64_t row0 = row_of(it);
-    if (!kHold || it + 1 < kIters) {
-      bwd_compute<T, D, U, kFull, false>(buf[it % kDepth], dx + row0 * pt.dx,
-                                         dg + row0 * pt.dg, pt, wf, eps, lane,
-                                         nvalid_of(it), acc, held);
-    } else {
-      held.row0 = row0;
-      held.nvalid = nvalid_of(it);
-      bwd_compute<T, D, U, kFull, true>(buf[it % kDepth], dx + row0 * pt.dx,
-                                        dg + row0 * pt.dg, pt, wf, eps, lane,
-                                        held.nvalid, acc, held);
+    for (int it = 0; it < kIters; ++it) {
+      const int ahead = it + kDepth - 1;
+      if (ahead < kIters) load(buf[ahead % kDepth], ahead);
+      const int64_t row0 = row_of(it);
+      if (!kHold || it + 1 < kIters) {
+        bwd_compute<T, D, U, kFull, false>(buf[it % kDepth], dx + row0 * pt.dx,
+                                           dg + row0 * pt.dg, pt, wf, eps, lane,
+                                           nvalid_of(it), acc, held);
+      } else {
+        held.row0 = row0;
+        held.nvalid = nvalid_of(it);
+        bwd_compute<T, D, U, kFull, true>(buf[it % kDepth], dx + row0 * pt.dx,
+                                          dg + row0 * pt.dg, pt, wf, eps, lane,
+                                          held.nvalid, acc, held);
+      }
     }
   }
 }
 
-// Cross-workgroup hand-off of the dw partials.  A partial is written with
-// device-scope (write-through) stores, each wave waits until its stores are
-// complete, and only then does one thread bump the arrival counter; the
-// workgroup that sees itself last reads the partials with device-scope loads
-// (which do not hit stale lines in the per-XCD L2).  No cache-wide write-back
-// or invalidation is needed, so the streaming of dx and dg is not disturbed.
+// Cross-workgroup hand-off of the dw partials, and why its order holds.
+//
+// Producer (the workgroup of chunk c):
+//   1. each of threads 0..D-1 writes its column of partial[c] with a relaxed
+//      agent-scope atomic store (store_coherent: global_store_dword sc1 on
+//      gfx950, written through this XCD's L2 to the point where every XCD's
+//      accesses meet);
+//   2. s_waitcnt vmcnt(0) (wait_memory): the wave waits until those stores
+//      are acknowledged, which for an sc1 store means the value is visible
+//      to agent-scope accesses from any XCD;
+//   3. __syncthreads(), so every storing wave has passed step 2;
+//   4. thread 0 increments the group's counter (relaxed agent-scope atomic
+//      add that returns the old value: global_atomic_add sc0).
+// Consumer (the workgroup whose increment was the group's last):
+//   5. it has waited for the atomic's returned value (s_waitcnt) and branched
+//      on it through LDS and a barrier before it issues any load of the
+//      partials; GPUs issue no load ahead of such a branch;
+//   6. it reads the partials with agent-scope loads (buffer_load sc1), which
+//      are served at the same point of coherence, never from a stale line of
+//      its own XCD's L2 (a line left, e.g., by an earlier call that used
+//      the same workspace).
+// Every producer's increment is ordered after its partial is visible (2-4),
+// and the last increment follows all others in the counter's modification
+// order, so the consumer's loads (5-6) see every partial of the group.  The
+// same holds one level up (group sums -> overall counter -> final sum).
+// This is the sequence the compiler's own agent-scope release/acquire
+// lowering for gfx950 produces (release: s_waitcnt vmcnt(0) before the
+// atomic; acquire: wait for the atomic, then coherent loads), minus the
+// cache-wide L2 write-back (buffer_wbl2) and invalidate (buffer_inv) that
+// such a fence adds for plain stores and loads elsewhere in the wave: the
+// partials are themselves agent-scope atomic accesses and need neither.  A
+// version with __threadfence() (both cache-wide operations per workgroup)
+// ran 5x slower.  What it relies on: sc1 stores and loads and the vmcnt
+// wait behave as above (gfx942/gfx950 memory model); the compiler does not
+// move the stores past wait_memory (an s_waitcnt builtin, a barrier to it)
+// nor the loads above the branch on the atomic's result.  The 200-run soak
+// (tests/test_handoff_soak.py) and the 10-run bitwise tests check it on the
+// device.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -723,6 +926,10 @@ bwd_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ g,
     } else {
       bwd_chunk<T, D, U, kWaves, R, kPrefetch, kHold, kLbs, false>(
           x, g, dy, dx, dg, pt, wf, eps, cb.row0, cb.stride, rows, wave, lane, acc, held);
+    }
+    if (can_overflow<T, D>() && wave_any_nan(acc[0])) {
+      bwd_chunk_fixup<T, D, U, kWaves, R, kHold, false>(x, g, dy, dx, dg, pt, wf, eps, cb.row0,
+                                                        cb.stride, rows, wave, lane, acc, held);
     }
     const int contrib = wave * S::kRows + sub;
 #pragma unroll

@@ -80,8 +80,8 @@ def test_dtype_width_parity(dname, D, rows):
         _check_dw(dw, dw_ref, dtype, dw_fp32)
 
 
-@pytest.mark.parametrize("D", [64, 256])
-@pytest.mark.parametrize("dname", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dname", ["bf16", "f16", "f32"])
 def test_dtype_width_paths(dname, D):
     """Checkpointed step, non-deterministic dw and strided rows reach the
     same instantiations: step equals fwd + bwd bitwise, strided rows equal
