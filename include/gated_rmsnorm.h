@@ -96,7 +96,11 @@ typedef enum grn_status {
     GRN_ERR_WORKSPACE = 6, /* workspace missing or smaller than required     */
     GRN_ERR_EPS = 7,       /* eps is negative, infinite or NaN               */
     GRN_ERR_HIP = 8,       /* the HIP runtime reported a launch error        */
-    GRN_ERR_ARG = 9        /* a flag argument (deterministic) is not 0 or 1  */
+    GRN_ERR_ARG = 9,       /* a flag argument (deterministic) is not 0 or 1,
+                              or (gated_rmsnorm_bwd_noalloc) the stream does
+                              not belong to the current device              */
+    GRN_ERR_SCRATCH = 10   /* gated_rmsnorm_bwd_noalloc: the call needs more
+                              than GRN_NOALLOC_SCRATCH_BYTES of workspace    */
 } grn_status;
 
 enum { GRN_DTYPE_BF16 = 0, GRN_DTYPE_F16 = 1, GRN_DTYPE_F32 = 2 };
@@ -211,6 +215,33 @@ grn_status gated_rmsnorm_ckpt_step_strided(
     void *workspace, size_t workspace_bytes, int64_t rows, int32_t D,
     float eps, int32_t dtype, int32_t dw_fp32, int32_t deterministic,
     void *stream);
+
+/* The backward of gated_rmsnorm_bwd, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same arguments without the workspace, the
+ * same kernels and the same output bits.  Its workspace is a static device
+ * array inside the library, GRN_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which
+ * each GPU the library runs on holds from the library's loading until the
+ * process ends.  A call whose gated_rmsnorm_workspace_bytes-style need
+ * (counters and partials for `rows` rows of D values of `dtype`; about
+ * 4 bytes per row at D = 128, so up to about 16.7 million such rows) exceeds
+ * that size returns GRN_ERR_SCRATCH and enqueues nothing.
+ *
+ * The stream must belong to the calling thread's current device (else
+ * GRN_ERR_ARG).  The first call on a device looks up that device's copy of
+ * the array and enqueues a small kernel on `stream` that zeroes its arrival
+ * counters; every completed backward leaves them at zero again.  All calls on
+ * one GPU share its array, which keeps the last call's contents: two calls
+ * whose work overlaps on one GPU (other streams, other threads, graphs
+ * replayed concurrently) race and may give a wrong dw; serialize them, or
+ * use gated_rmsnorm_bwd with one workspace each.  Allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine. */
+#define GRN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+grn_status gated_rmsnorm_bwd_noalloc(const void *x, const void *g, const void *w,
+                                     const void *dy, void *dx, void *dg, void *dw,
+                                     int64_t rows, int32_t D, float eps,
+                                     int32_t dtype, int32_t dw_fp32, void *stream);
 
 /* Zero the arrival counters at the front of a workspace (the first
  * gated_rmsnorm_workspace_init_bytes() bytes) by enqueueing a small kernel

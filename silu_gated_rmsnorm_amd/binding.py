@@ -72,6 +72,10 @@ _SIGS = {
                                                           ctypes.c_float, ctypes.c_int32,
                                                           ctypes.c_int32, ctypes.c_int32,
                                                           _VP]),
+    "gated_rmsnorm_bwd_noalloc": (ctypes.c_int32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                    ctypes.c_int64, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.c_int32,
+                                                    ctypes.c_int32, _VP]),
     "gated_rmsnorm_workspace_init": (ctypes.c_int32, [_VP, ctypes.c_size_t, _VP]),
     "gated_rmsnorm_workspace_init_bytes": (ctypes.c_size_t, []),
     "gated_rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -231,6 +235,26 @@ def gated_rmsnorm_bwd(x, g, w, dy, eps: float = 1e-6, dw_fp32: bool = False,
                                            float(eps), dt, int(bool(dw_fp32)),
                                            int(bool(deterministic)), _stream(x))
     _check(st)
+    return dx, dg, dw
+
+
+def gated_rmsnorm_bwd_noalloc(x, g, w, dy, dx, dg, dw, eps: float = 1e-6):
+    """gated_rmsnorm_bwd on the library's static scratch (no workspace): for
+    callers that cannot allocate.  x, g, dy, dx, dg are packed [rows, D]
+    tensors; dw is an FP32 or x-typed [D] tensor (its dtype selects dw_fp32).
+    Returns (dx, dg, dw).  Calls that overlap on one GPU share the scratch."""
+    lib = load_library()
+    (px, sx) = _act("x", x)
+    rows, D = x.shape
+    (pg, sg), pw = _act("g", g, x), _weight(w, x)
+    pdy, sdy = _act("dy", dy, x)
+    (pdx, sdx), (pdg, sdg) = _act("dx", dx, x), _act("dg", dg, x)
+    if not (sx == sg == sdy == sdx == sdg == D):
+        raise ValueError("gated_rmsnorm_bwd_noalloc takes packed rows only")
+    dw_fp32 = dw.dtype == torch.float32 and x.dtype != torch.float32
+    dw = _dw(dw, dw_fp32, x)
+    _check(lib.gated_rmsnorm_bwd_noalloc(px, pg, pw, pdy, pdx, pdg, dw.data_ptr(), rows, D,
+                                         float(eps), _dtype_code(x), int(dw_fp32), _stream(x)))
     return dx, dg, dw
 
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 
 namespace {
 
@@ -157,6 +158,44 @@ size_t dw_size(int32_t D, int32_t dtype, int32_t dw_fp32) {
 
 grn_status hip_status(hipError_t e) { return e == hipSuccess ? GRN_OK : GRN_ERR_HIP; }
 
+// ---------------------------------------------------------------------------
+// Scratch of gated_rmsnorm_bwd_noalloc: the backward's workspace (arrival
+// counters, then the dw partials) in a static device array, one copy per
+// GPU, held from the library's loading until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the device
+// address is fetched once per device with hipGetSymbolAddress and only that
+// address is ever handed to a kernel.
+static_assert(GRN_NOALLOC_SCRATCH_BYTES % 256 == 0, "a whole number of 256-byte blocks");
+static __device__ __align__(256) unsigned char scratch[GRN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;                 // device address of this device's copy
+  hipError_t err = hipErrorNotInitialized;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch, set up on this device's
+// first call: hipGetSymbolAddress, then the arrival counters zeroed by a
+// small kernel enqueued on `s` (no memset: the call may be under graph
+// capture).  Every completed backward leaves the counters at zero again.
+hipError_t scratch_for(int dev, hipStream_t s, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p == nullptr) e = hipErrorInvalidSymbol;
+    if (e == hipSuccess) e = grn::launch_counters_zero(p, s);
+    slot.ptr = e == hipSuccess ? p : nullptr;
+    slot.err = e;
+  });
+  *out = slot.ptr;
+  return slot.err;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +280,36 @@ grn_status gated_rmsnorm_bwd(const void* x, const void* g, const void* w,
                                    dtype, dw_fp32, 1, stream);
 }
 
+grn_status gated_rmsnorm_bwd_noalloc(const void* x, const void* g, const void* w,
+                                     const void* dy, void* dx, void* dg, void* dw,
+                                     int64_t rows, int32_t D, float eps, int32_t dtype,
+                                     int32_t dw_fp32, void* stream) {
+  grn_status st = check_common(rows, D, dtype);
+  if (st != GRN_OK) return st;
+  if (dw_fp32 != 0 && dw_fp32 != 1) return GRN_ERR_DTYPE;
+  if ((st = check_eps(eps)) != GRN_OK) return st;
+  const size_t need = workspace_need(rows, D, (int32_t)elem_bytes(dtype));
+  if (need > (size_t)GRN_NOALLOC_SCRATCH_BYTES) return GRN_ERR_SCRATCH;
+  const Act acts[5] = {{x, D}, {g, D}, {dy, D}, {dx, D}, {dg, D}};
+  st = check_buffers(rows, D, elem_bytes(dtype), acts, 5, 3, w, nullptr, 0, dw,
+                     dw_size(D, dtype, dw_fp32));
+  if (st != GRN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GRN_ERR_HIP;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return GRN_ERR_HIP;
+    if ((int)sdev != dev) return GRN_ERR_ARG;
+  }
+  void* ws = nullptr;
+  if (scratch_for(dev, s, &ws) != hipSuccess) return GRN_ERR_HIP;
+  grn::RowStrides rs;
+  rs.x = rs.g = rs.dy = rs.dx = rs.dg = D;
+  return hip_status(grn::launch_bwd(x, g, w, dy, dx, dg, dw, dw_fp32, 1, ws, rs, rows, D,
+                                    dtype, eps, env_max_wg(), s));
+}
+
 grn_status gated_rmsnorm_ckpt_step_strided(
     const void* x, int64_t x_stride, const void* g, int64_t g_stride,
     const void* w, const void* dy, int64_t dy_stride, void* y, int64_t y_stride,
@@ -314,7 +383,8 @@ const char* gated_rmsnorm_status_string(int32_t status) {
     case GRN_ERR_WORKSPACE: return "GRN_ERR_WORKSPACE: workspace missing or too small";
     case GRN_ERR_EPS: return "GRN_ERR_EPS: eps must be finite and >= 0";
     case GRN_ERR_HIP: return "GRN_ERR_HIP: the HIP runtime reported a launch error";
-    case GRN_ERR_ARG: return "GRN_ERR_ARG: a flag argument is not 0 or 1";
+    case GRN_ERR_ARG: return "GRN_ERR_ARG: a flag argument is not 0 or 1, or the stream is not on the current device";
+    case GRN_ERR_SCRATCH: return "GRN_ERR_SCRATCH: the call needs more workspace than the library's static scratch holds (GRN_NOALLOC_SCRATCH_BYTES; use gated_rmsnorm_bwd with a workspace)";
     default: return "unknown gated_rmsnorm status";
   }
 }

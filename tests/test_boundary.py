@@ -17,7 +17,7 @@ from silu_gated_rmsnorm_amd import binding
 ROOT = pathlib.Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "gated_rmsnorm.h"
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, EPS, HIP, ARG = range(10)
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, EPS, HIP, ARG, SCRATCH = range(11)
 ROWS = 10
 ACT = ROWS * 128 * 2            # bytes of one [10, 128] BF16 tensor
 BASE = 0x7F0000000000           # fake device addresses, 4 KiB apart
@@ -44,7 +44,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert sorted(binding._SIGS) == names
@@ -229,3 +229,45 @@ def test_binding_rejects_cpu_tensors():
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         binding.load_library(tmp_path / "nope.so")
+
+
+def test_noalloc_rejects_before_any_launch(lib):
+    """gated_rmsnorm_bwd_noalloc checks every argument, and that the call
+    fits the static scratch (GRN_NOALLOC_SCRATCH_BYTES = 64 MiB), before any
+    HIP call: these fake pointers are never touched."""
+    f = lib.gated_rmsnorm_bwd_noalloc
+    eps = 1e-6
+    header = HEADER.read_text()
+    assert "#define GRN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in header
+    cap = 64 << 20
+    # the largest BF16 D = 128 call that fits, and the first that does not
+    C = lib.gated_rmsnorm_workspace_init_bytes()
+
+    def need(rows, D=128, R=128):
+        chunks = math.ceil(rows / R)
+        gs = math.isqrt(chunks - 1) + 1 if chunks > 1 else 1
+        return C + (chunks + math.ceil(chunks / gs)) * 4 * D
+
+    lo, hi = 1, 1 << 26
+    while lo < hi:                       # largest rows with need(rows) <= cap
+        mid = (lo + hi + 1) // 2
+        if need(mid) <= cap:
+            lo = mid
+        else:
+            hi = mid - 1
+    assert 16_000_000 < lo < 17_000_000
+    assert f(X, G, W, DY, DX, DG, DW, lo + 1, 128, eps, 0, 0, None) == SCRATCH
+    assert f(X, G, W, DY, DX, DG, DW, 12582912 * 2, 128, eps, 0, 1, None) == SCRATCH
+    # D = 256 needs twice the bytes per chunk
+    assert f(X, G, W, DY, DX, DG, DW, lo, 256, eps, 0, 0, None) == SCRATCH
+    assert f(X, G, W, DY, DX, DG, DW, 10, 96, eps, 0, 0, None) == SHAPE
+    assert f(X, G, W, DY, DX, DG, DW, -1, 128, eps, 0, 0, None) == SHAPE
+    assert f(X, G, W, DY, DX, DG, DW, 10, 128, eps, 7, 0, None) == DTYPE
+    assert f(X, G, W, DY, DX, DG, DW, 10, 128, eps, 0, 2, None) == DTYPE
+    assert f(X, G, W, DY, DX, DG, DW, 10, 128, -1.0, 0, 0, None) == EPS
+    assert f(X, G, None, DY, DX, DG, DW, 10, 128, eps, 0, 0, None) == NULL
+    assert f(X, G, W, DY, DX, DG, None, 10, 128, eps, 0, 0, None) == NULL
+    assert f(X, G, W, DY, X, DG, DW, 10, 128, eps, 0, 0, None) == ALIAS
+    assert f(X + 8, G, W, DY, DX, DG, DW, 10, 128, eps, 0, 0, None) == ALIGN
+    assert b"GRN_ERR_SCRATCH" in lib.gated_rmsnorm_status_string(SCRATCH)
+
