@@ -267,8 +267,9 @@ class Workbench:
 
     def graph_time(self, fn, n):
         """GPU time per operation: n operations (rotating over the sets)
-        captured into one HIP graph and replayed once, so the host's launch
-        and submission costs drop out and the launches run back to back.
+        captured into one HIP graph; after one untimed replay, the median of
+        three timed replays.  The host's launch and submission costs drop out
+        and the launches run back to back.
         This is the figure comparable to the pages' graph timings (kernel
         time of ops replayed from a graph)."""
         torch = self.torch
@@ -280,14 +281,17 @@ class Workbench:
                 fn(self.sets[i % self.nsets])
         gr.replay()
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        gr.replay()
-        b.record()
-        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / n)
         del gr
-        return a.elapsed_time(b) * 1e3 / n
+        return sorted(times)[1]
 
     def replay_wall(self, fn, reps):
         """Wall time per replay of a graph that holds one operation (one graph
