@@ -350,7 +350,7 @@ def side_workload(torch, binding, name, dev, settle_s):
            "timing": "GPU time per operation: N operations captured in one HIP graph, "
                      "buffer sets rotated"}
     ops = {}
-    n = max(2 * wb.nsets, 20)
+    n = max(2 * wb.nsets, 100)
     if name == "1031x48":
         wb.settle(lambda st: wb.op_step(st), settle_s)
         ops["fwd"] = rate(wb.graph_time(wb.op_fwd, n), wb.fwd_bytes)
@@ -495,7 +495,7 @@ def main():
         # operation from N operations captured in one graph.  Wall time per
         # replay of a one-operation graph (one submission each) is reported
         # as *_replay_wall.
-        nb = max(2 * nsets, 20)
+        nb = max(2 * nsets, 100)
         kinds = {"fwdg": (wb.op_fwd, wb.fwd_bytes), "bwdg": (wb.op_bwd, wb.bwd_bytes),
                  "bwdg_f32": (lambda st: wb.op_bwd(st, True), wb.bwd32_bytes),
                  "bwdg_nondet": (lambda st: wb.op_bwd(st, False, False), wb.bwd_bytes),
