@@ -62,8 +62,10 @@
  *  - Errors: arguments are checked before anything is enqueued; an invalid
  *    call returns a non-zero grn_status and enqueues nothing.  A failed
  *    launch returns GRN_ERR_HIP.  Nothing is thrown across the ABI.
- *  - Threads: the library holds no mutable state; concurrent calls are safe
- *    if they share no output or workspace.
+ *  - Threads: the library's only mutable state is the static scratch of
+ *    gated_rmsnorm_bwd_noalloc (see there); every other call is safe to make
+ *    concurrently, from any thread and on any stream, if the calls share no
+ *    output or workspace.
  *  - Launch shape: the environment variable GATED_RMSNORM_MAX_WG, when set
  *    to a positive integer, caps the number of workgroups per launch (a
  *    tuning and testing knob).  Results do not depend on it.
