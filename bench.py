@@ -457,6 +457,7 @@ def main():
     ops = {}
     roofline = None
     apart = None
+    runtime_copy = None
     if not args.no_ops:
         R = args.op_reps
 
@@ -545,6 +546,23 @@ def main():
                     "traffic": traffic_from_counters(wl.name) if default_shape else None,
                     "bytes_per_launch": wb.bwd_bytes, "avg_us": round(bwd_us, 3)}
 
+        # Context next to the 8 TB/s peak: what the HIP runtime's own
+        # device-to-device copy of one tensor (1 read + 1 write) reaches on
+        # this GPU with the same rotation of buffer sets.  Not a ceiling: the
+        # kernels here stream faster than it.
+        if args.layout == "packed":
+            def copy_one(st):
+                st["dx"].copy_(st["x"])
+
+            wb.settle(copy_one, settle_s)
+            copy_us = wb.rotate_time(copy_one, R)
+            runtime_copy = dict(rate(copy_us, 2 * wb.tensor_bytes),
+                                kind=f"device-to-device copy of one {wb.tensor_bytes}-byte tensor "
+                                     "by the HIP runtime (torch copy_; 1 read + 1 write), buffer "
+                                     f"sets rotated, mean over {R} copies")
+            log(f"[bench] runtime copy {copy_us:9.2f} us {runtime_copy['GB/s']:8.1f} GB/s "
+                f"{100 * runtime_copy['frac']:5.1f}%")
+
     cpu = None
     if not args.no_cpu_baseline and args.dtype == "bf16":
         cpu = cpu_baseline(wb.inp, wl, wb.step_bytes, args.cpu_seconds)
@@ -584,6 +602,7 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "fwd_plus_bwd_apart": apart,
         "roofline": roofline,
+        "runtime_copy": runtime_copy,
         "cpu_baseline": cpu,
         "ops": ops,
         "workloads": workloads,
